@@ -1,0 +1,331 @@
+"""Pins of the CPU oracle against things other than itself: worked examples
+(tests/golden), textbook/library routines, closed forms, invariants and brute
+force.  Each test cites the passage of the pages (or the reading) it checks.
+A negative control plants a mistake in a copy of an oracle step, on the CPU,
+and shows the pin catches it.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle.twl_oracle as O
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# ---------------------------------------------------------------- FWHT ------
+
+def test_fwht_worked_example_n4():
+    # tests/golden/fwht4.txt: hand-worked H4 product ([P1] section 1 recursion).
+    lines = dict(ln.split(":", 1) for ln in _golden_lines("fwht4.txt"))
+    x = np.array(lines["input"].split(), dtype=np.float32)
+    want = np.array(lines["output"].split(), dtype=np.float32)
+    assert np.array_equal(O.fwht_f32(x, 4), want)
+
+
+def test_fwht_identity_is_sylvester_hadamard():
+    # Textbook/library routine: scipy.linalg.hadamard builds H_n by the Sylvester
+    # recursion; FWHT of the identity must reproduce it exactly.
+    for n in (2, 8, 64, 1024):
+        H = O.fwht_f32(np.eye(n, dtype=np.float32), n)
+        assert np.array_equal(H, scipy.linalg.hadamard(n).astype(np.float32)), n
+
+
+def test_hadamard_orthogonality():
+    # H H^T = n I (spec pin; exact for integer entries).
+    H = O.fwht_f32(np.eye(1024, dtype=np.float32), 1024).astype(np.float64)
+    assert np.array_equal(H @ H.T, 1024.0 * np.eye(1024))
+
+
+def _sylvester_split_holds(fwht):
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((64, 1024)) * 3).astype(np.float32)
+    full = fwht(x, 1024)
+    a = fwht(x[:, :512], 512)
+    b = fwht(x[:, 512:], 512)
+    want = np.concatenate([a + b, a - b], axis=1)     # fp32 sum / difference
+    return np.array_equal(full, want)
+
+
+def test_fwht_last_stage_is_the_pages_recursion_bitwise():
+    # [P1] section 1: H1024 [a; b] = [H512 a + H512 b ; H512 a - H512 b], and the
+    # kernel's final butterfly stage has this form -> ascending stage order.
+    # Bitwise in fp32, which pins the order of the floating-point DAG (R3).
+    assert _sylvester_split_holds(O.fwht_f32)
+
+
+def _fwht_descending(v, n):
+    """Planted mistake (negative control): same butterflies, descending order."""
+    v = np.array(v, dtype=np.float32, copy=True)
+    lead = v.shape[:-1]
+    nb = v.shape[-1] // n
+    h = n // 2
+    while h >= 1:
+        w = v.reshape(lead + (nb, n // (2 * h), 2, h))
+        lo = w[..., 0, :].copy()
+        hi = w[..., 1, :].copy()
+        w[..., 0, :] = lo + hi
+        w[..., 1, :] = lo - hi
+        v = w.reshape(lead + (nb * n,))
+        h //= 2
+    return v
+
+
+def test_negative_control_descending_fwht_fails_the_split_pin():
+    # Mirrors the rank-swap control of [P1] section 1: the pin must detect a
+    # wrong (but mathematically equivalent in exact arithmetic) DAG.
+    assert not _sylvester_split_holds(_fwht_descending)
+    # ... while both agree to fp32 rounding, so only the bitwise pin sees it.
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((8, 1024)).astype(np.float32)
+    np.testing.assert_allclose(_fwht_descending(x, 1024), O.fwht_f32(x, 1024), rtol=0, atol=1e-4)
+
+
+def test_fwht_involution_small_integers():
+    # H H = n I, so applying the transform twice to small integers is exact.
+    rng = np.random.default_rng(7)
+    x = rng.integers(-50, 51, size=(4, 2048)).astype(np.float32)
+    assert np.array_equal(O.fwht_f32(O.fwht_f32(x)), 1024 * x)
+
+
+def test_fwht_f32_close_to_dense_f64():
+    H = scipy.linalg.hadamard(1024).astype(np.float64)
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((16, 1024)).astype(np.float32)
+    ref = x.astype(np.float64) @ H.T
+    got = O.fwht_f32(x).astype(np.float64)
+    assert np.max(np.abs(got - ref)) <= 1e-6 * np.max(np.abs(ref)) * 10
+
+
+def test_rotation_is_orthonormal_and_signed():
+    # R1/R2: r = (1/32) H (sign*x) per block -> norms preserved per block, and
+    # the sign table acts before H (indexed by the full input channel).
+    layer = W.make_layer(11, 4, 2048, 8)
+    r = O.rotate(layer.x_bits, layer.sign).astype(np.float64)
+    x = O.bf16_to_f32(layer.x_bits).astype(np.float64)
+    for blk in range(2):
+        sl = slice(1024 * blk, 1024 * (blk + 1))
+        np.testing.assert_allclose(np.linalg.norm(r[:, sl], axis=1), np.linalg.norm(x[:, sl], axis=1), rtol=1e-5)
+    H = scipy.linalg.hadamard(1024).astype(np.float64) / 32.0
+    ref = (x[:, 1024:] * layer.sign[1024:]) @ H.T
+    np.testing.assert_allclose(r[:, 1024:], ref, rtol=0, atol=1e-5 * np.abs(ref).max())
+
+
+# ------------------------------------------------------- quantisation -------
+
+def test_quantise_worked_examples():
+    for ln in _golden_lines("quantise_row.txt"):
+        rs, sc, qs = [p.split() for p in ln.split("|")]
+        r = np.array([rs], dtype=np.float32)
+        x_i8, a_scale = O.quantise_per_token(r)
+        assert a_scale[0] == np.float32(sc[0])
+        assert x_i8[0].tolist() == [int(v) for v in qs]
+
+
+def test_quantise_invariants_on_config_tiny():
+    layer = W.make_config("tiny")
+    r = O.rotate(layer.x_bits, layer.sign)
+    x_i8, a_scale = O.rotate_quant_act(layer.x_bits, layer.sign)
+    assert x_i8.dtype == np.int8 and a_scale.dtype == np.float32
+    assert np.all(np.abs(x_i8.astype(np.int32)) <= 127)
+    assert np.all(np.max(np.abs(x_i8.astype(np.int32)), axis=1) == 127)
+    # reconstruction error within half a step (plus fp32 rounding slack)
+    err = np.abs(x_i8.astype(np.float64) * a_scale[:, None] - r.astype(np.float64))
+    assert np.all(err <= a_scale[:, None] * (0.5 + 1e-5))
+    # a_scale tracks the row absmax exactly
+    assert np.array_equal(a_scale, (np.max(np.abs(r), axis=1) / np.float32(127)).astype(np.float32))
+
+
+def test_quantise_invariant_to_the_rotation_normalisation():
+    # R1: the 1/32 factor is a power of two, so x_i8 is unchanged and a_scale
+    # scales by exactly 32 if the rotation is left unnormalised.
+    layer = W.make_config("tiny")
+    r = O.rotate(layer.x_bits, layer.sign)
+    x1, s1 = O.quantise_per_token(r)
+    x2, s2 = O.quantise_per_token(r * np.float32(32))
+    assert np.array_equal(x1, x2) and np.array_equal(s1 * np.float32(32), s2)
+
+
+def test_quantise_zero_token():
+    x_bits = np.zeros((2, 1024), dtype=np.uint16)
+    x_bits[1, 5] = W.f32_to_bf16_bits(np.array([1.5], dtype=np.float32))[0]
+    sign = np.ones(1024, dtype=np.int8)
+    x_i8, a_scale = O.rotate_quant_act(x_bits, sign)
+    assert a_scale[0] == 0 and not x_i8[0].any()
+    # a single spike rotates to a flat +-1.5/32 row -> every code is +-127
+    assert np.all(np.abs(x_i8[1].astype(np.int32)) == 127)
+
+
+# --------------------------------------------------------------- scales -----
+
+def test_scale_decomposition_worked_examples():
+    for ln in _golden_lines("scale_ratio.txt"):
+        ss, sm, qs = [p.split() for p in ln.split("|")]
+        s_bits = np.array([ss], dtype=np.float16).view(np.uint16)
+        q, smax = O.decompose_scales(s_bits)
+        assert smax[0] == np.float32(sm[0])
+        assert q[0].tolist() == [int(v) for v in qs]
+
+
+def _exact_round_half_even(fr: Fraction) -> int:
+    fl = fr.numerator // fr.denominator
+    rem = fr - fl
+    if rem > Fraction(1, 2):
+        return fl + 1
+    if rem < Fraction(1, 2):
+        return fl
+    return fl if fl % 2 == 0 else fl + 1
+
+
+def test_scale_decomposition_matches_exact_rationals():
+    # R8: rint(fl32(127 s) / smax) in fp32 agrees with the exact rational
+    # round(127 s / smax) on the workload's scales; report the exact ties.
+    layer = W.make_layer(12, 1, 1024, 2048)
+    q, smax = O.decompose_scales(layer.s_bits)
+    s = layer.s.astype(np.float64)
+    ties = 0
+    for n in range(s.shape[0]):
+        sm = Fraction(float(smax[n]))
+        for g in range(s.shape[1]):
+            fr = Fraction(127) * Fraction(float(s[n, g])) / sm
+            ties += fr.denominator == 2
+            assert q[n, g] == _exact_round_half_even(fr), (n, g)
+    assert ties > 0          # the sample exercises the ties-to-even rule (15 exact ties)
+
+
+def test_scale_invariants():
+    layer = W.make_config("tiny")
+    q, smax = O.decompose_scales(layer.s_bits)
+    assert np.all(np.abs(q.astype(np.int32)) <= 127)                  # [P1] s.4: fits int8
+    assert np.all(np.max(q.astype(np.int32), axis=1) == 127)
+    s = layer.s.astype(np.float64)
+    recon = q.astype(np.float64) * smax[:, None].astype(np.float64) / 127.0
+    assert np.all(np.abs(recon - s) <= smax[:, None] / 254.0 * (1 + 1e-6))
+
+
+# -------------------------------------------------------------- packing -----
+
+def test_pack_worked_example():
+    lines = dict(ln.split(":", 1) for ln in _golden_lines("pack_word.txt"))
+    code = np.array([lines["codes"].split()], dtype=np.int8)
+    want = [int(b, 16) for b in lines["bytes"].split()]
+    assert O.pack_codes(code)[0].tolist() == want
+
+
+def test_pack_roundtrip_and_size():
+    layer = W.make_layer(13, 1, 2048, 33, codes="sparse40")
+    p = O.pack_codes(layer.code)
+    assert p.shape == (33, 2048 // 4) and p.dtype == np.uint8
+    assert np.array_equal(O.unpack_codes(p, 2048), layer.code)
+    words = p.view("<u4")
+    for i in range(16):                       # no 2-bit field holds 0b11
+        assert not np.any(((words >> (2 * i)) & 3) == 3)
+
+
+def test_pack_rejects_bad_codes():
+    with pytest.raises(ValueError):
+        O.pack_codes(np.full((1, 16), 2, dtype=np.int8))
+
+
+# ------------------------------------------------------ GEMM and epilogue ---
+
+def _brute_acc(x_i8, code, q):
+    M, K = x_i8.shape
+    N = code.shape[0]
+    acc = np.zeros((M, N), dtype=np.int64)
+    for t in range(M):
+        for n in range(N):
+            s = 0
+            for k in range(K):
+                s += int(x_i8[t, k]) * int(code[n, k]) * int(q[n, k // 128])
+            acc[t, n] = s
+    return acc
+
+
+@pytest.mark.parametrize("M,N", [(1, 1), (3, 5)])
+def test_acc_brute_force_tiny(M, N):
+    layer = W.make_layer(14 + M, M, 1024, N)
+    x_i8, _ = O.rotate_quant_act(layer.x_bits, layer.sign)
+    q, _ = O.decompose_scales(layer.s_bits)
+    assert np.array_equal(O.linear_acc(x_i8, layer.code, q), _brute_acc(x_i8, layer.code, q))
+
+
+def test_acc_group_sum_identity_and_bound():
+    # sum_g q[n,g] * sum_{k in g} code*x == acc  (integer identity), |acc| <= 127^2 K
+    layer = W.make_config("tiny")
+    x_i8, _ = O.rotate_quant_act(layer.x_bits, layer.sign)
+    q, _ = O.decompose_scales(layer.s_bits)
+    acc = O.linear_acc(x_i8, layer.code, q).astype(np.int64)
+    xg = x_i8.astype(np.int64).reshape(16, 8, 128)
+    cg = layer.code.astype(np.int64).reshape(256, 8, 128)
+    part = np.einsum("tgk,ngk->tng", xg, cg)
+    assert np.array_equal((part * q.astype(np.int64)[None]).sum(-1), acc)
+    assert np.all(np.abs(acc) <= 127 * 127 * 1024)
+
+
+def test_acc_sampled_matches_full():
+    layer = W.make_config("tiny")
+    x_i8, _ = O.rotate_quant_act(layer.x_bits, layer.sign)
+    q, _ = O.decompose_scales(layer.s_bits)
+    acc = O.linear_acc(x_i8, layer.code, q)
+    rows = np.array([0, 3, 15, 7])
+    cols = np.array([255, 0, 128, 77])
+    assert np.array_equal(O.linear_acc_at(x_i8, layer.code, q, rows, cols), acc[rows, cols])
+
+
+def test_epilogue_closed_form():
+    acc = np.array([[127, -254], [0, 1]], dtype=np.int32)
+    a_scale = np.array([0.5, 2.0], dtype=np.float32)
+    smax = np.array([1.0, 0.25], dtype=np.float32)
+    y = O.epilogue(acc, a_scale, smax)
+    want = np.array([[0.5, -0.25], [0.0, 0.5 / 127.0]], dtype=np.float64).astype(np.float32)
+    assert np.array_equal(y, want)
+
+
+# ----------------------------------------------------- end-to-end sanity ----
+
+def test_relative_error_vs_unquantised_is_about_1e2():
+    # [P1] section 4 reports 9.5e-3 per layer for the int8 path.  Sanity, not parity.
+    layer = W.make_config("tiny")
+    x_i8, a_scale = O.rotate_quant_act(layer.x_bits, layer.sign)
+    q, smax = O.decompose_scales(layer.s_bits)
+    y = O.ternary_linear(x_i8, a_scale, layer.code, q, smax)
+    e = O.rel_err(y, O.float_reference(layer.x_bits, layer.sign, layer.code, layer.s_bits))
+    assert 3e-3 < e < 2.5e-2, e
+
+
+def test_negative_control_skipping_rotation_raises_error():
+    # "the rotation evens out outliers" ([P1] section 4): quantising without it
+    # must be clearly worse on the outlier workload.
+    layer = W.make_config("tiny")
+    q, smax = O.decompose_scales(layer.s_bits)
+    ref = O.float_reference(layer.x_bits, layer.sign, layer.code, layer.s_bits)
+    x_i8, a_scale = O.rotate_quant_act(layer.x_bits, layer.sign)
+    e_rot = O.rel_err(O.ternary_linear(x_i8, a_scale, layer.code, q, smax), ref)
+    # unrotated path: quantise x directly, weights in the unrotated basis
+    x = O.bf16_to_f32(layer.x_bits)
+    xn, an = O.quantise_per_token(x)
+    H = scipy.linalg.hadamard(1024).astype(np.float64) / 32.0
+    w_rot = layer.code.astype(np.float64) * np.repeat(layer.s.astype(np.float64), 128, axis=1)
+    w_plain = (w_rot @ H) * layer.sign[None, :]          # same linear map, input basis
+    y_plain = (xn.astype(np.float64) * an[:, None]) @ w_plain.T
+    e_plain = O.rel_err(y_plain, ref)
+    assert e_plain > 2.5 * e_rot, (e_plain, e_rot)
+
+
+def test_negative_control_swapped_sign_blocks_gives_order_one_error():
+    layer = W.make_layer(21, 8, 2048, 64)
+    q, smax = O.decompose_scales(layer.s_bits)
+    ref = O.float_reference(layer.x_bits, layer.sign, layer.code, layer.s_bits)
+    bad = np.concatenate([layer.sign[1024:], layer.sign[:1024]])
+    x_i8, a_scale = O.rotate_quant_act(layer.x_bits, bad)
+    assert O.rel_err(O.ternary_linear(x_i8, a_scale, layer.code, q, smax), ref) > 0.5
