@@ -1,0 +1,330 @@
+#!/usr/bin/env python
+"""Benchmark of the ternary linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sections ...] [--no-cpu]
+
+Headline (the JSON `value`): one prefill step of the gate/up projection,
+M=512 tokens, K=5120, N=17408 -- rotate_quant_act followed by ternary_linear
+(int8-MFMA GEMM with fused 2-bit unpack and rescale) -- reported as int8 TOPS
+(2*M*N*K per step / step time).  Packing is a load-time operation and is done
+once before timing.  Inputs are seeded synthetic data with the pages' layer
+shapes; weights cycle through enough copies (>= 1.1 GB) that every step reads
+them from HBM rather than from the 256 MB last-level cache.
+
+Also measured and printed under "detail": the down projection (M=256,
+K=17408, N=5120), the decode sweep M in {1,4,8,16,24} over both layer shapes
+(weight GB/s), and the 64-layer stack (one 512-token prefill step and one
+24-token decode step), plus each kernel's own time from HIP events.
+
+"roofline" is for the dominant kernel (the prefill GEMM): achieved int8 TOP/s
+from its average event-timed duration against the 5.0 POP/s dense int8 MFMA
+peak.  "cpu_baseline" times the CPU oracle on the host (rank 0 only) on
+repeated full steps of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "int8 TOPS (prefill GEMM) + weight GB/s (decode GEMV), ms/step, % of roofline"
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+# VALU int8 dot4: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz x 4 MACs x 2 ops
+PEAK_VALU_DOT4_TOPS = 256 * 4 * 16 * 2.4e9 * 8 / 1e12
+CACHE_BUST_BYTES = int(1.1e9)
+SECTIONS = ("headline", "down", "decode", "stack")
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def weight_bytes(N: int, K: int) -> int:
+    return N * K // 4 + N * K // 128 + 4 * N
+
+
+class Timer:
+    """HIP-event timing of individual launches on torch's current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def __call__(self, key, fn):
+        ev0 = self.torch.cuda.Event(enable_timing=True)
+        ev1 = self.torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        out = fn()
+        ev1.record()
+        self.pairs.setdefault(key, []).append((ev0, ev1))
+        return out
+
+    def mean_ms(self, key):
+        ps = self.pairs.get(key, [])
+        if not ps:
+            return None
+        return sum(a.elapsed_time(b) for a, b in ps) / len(ps)
+
+    def reset(self):
+        self.pairs = {}
+
+
+def upload_layer(torch, twl, layer, copies: int):
+    """Host layer -> device x, sign and `copies` packed weight sets."""
+    x = torch.from_numpy(layer.x_bits.view("int16")).cuda()
+    sign = torch.from_numpy(layer.sign).cuda()
+    code = torch.from_numpy(layer.code).cuda()
+    s = torch.from_numpy(layer.s_bits.view("int16")).cuda()
+    packed, q, smax = twl.pack_ternary(code, s)
+    del code
+    sets = [(packed, q, smax)]
+    for _ in range(copies - 1):
+        sets.append((packed.clone(), q.clone(), smax.clone()))
+    return x, sign, sets
+
+
+def n_copies(N: int, K: int) -> int:
+    return max(1, -(-CACHE_BUST_BYTES // weight_bytes(N, K)))
+
+
+def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, timer):
+    """warmup + timed steps of rotate_quant_act + ternary_linear; returns ms/step."""
+    M, K = x.shape
+    N = sets[0][0].shape[0]
+    x_i8 = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    a_scale = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws_n = twl.workspace_bytes(M, N, K)
+    ws = torch.zeros(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+
+    def step(i, timed):
+        packed, q, smax = sets[i % len(sets)]
+        if timed:
+            timer("rotq", lambda: twl.rotate_quant_act(x, sign, out=(x_i8, a_scale)))
+            timer("linear", lambda: twl.ternary_linear(x_i8, a_scale, packed, q, smax, out=y,
+                                                        workspace=ws))
+        else:
+            twl.rotate_quant_act(x, sign, out=(x_i8, a_scale))
+            twl.ternary_linear(x_i8, a_scale, packed, q, smax, out=y, workspace=ws)
+
+    for i in range(warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def traffic_for(kernel_src: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    src = os.path.join(ROOT, "ternary_weight_linear_block_amd", "csrc", kernel_src)
+    if not (os.path.exists(path) and os.path.exists(src)):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    for ln in open(path):
+        p = ln.split()
+        if len(p) >= 5 and not ln.startswith("#") and p[0] == kernel_src and p[1] == workload:
+            if p[2] == sha:
+                return float(p[3]) + float(p[4])
+    return None
+
+
+def cpu_baseline(layer, min_s=10.0, max_reps=25):
+    """The CPU oracle as it stands, on repeated full steps of the workload."""
+    import numpy as np
+    import oracle.twl_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    q, smax = O.decompose_scales(layer.s_bits)     # load time, outside the timing
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        x_i8, a_scale = O.rotate_quant_act(layer.x_bits, layer.sign)
+        y = O.ternary_linear(x_i8, a_scale, layer.code, q, smax)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_s or reps >= max_reps:
+            break
+    ops = 2.0 * layer.M * layer.N * layer.K * reps
+    del y
+    return {"value": round(ops / el / 1e12, 4), "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} full steps (rotate_quant_act + ternary_linear, M={layer.M} K={layer.K} "
+                      f"N={layer.N}) in {el:.1f} s; numpy, BLAS threads={threads}, "
+                      f"affine cores={len(os.sched_getaffinity(0))}"}
+
+
+def section_layer(torch, twl, name, steps, warmup):
+    import workloads as W
+    layer = W.make_config(name)
+    x, sign, sets = upload_layer(torch, twl, layer, n_copies(layer.N, layer.K))
+    timer = Timer(torch)
+    ms = run_layer_steps(torch, twl, x, sign, sets, steps, warmup, timer)
+    lin = timer.mean_ms("linear")
+    rq = timer.mean_ms("rotq")
+    ops = 2.0 * layer.M * layer.N * layer.K
+    out = {"M": layer.M, "K": layer.K, "N": layer.N, "ms_per_step": round(ms, 5),
+           "step_tops": round(ops / ms / 1e9, 2), "linear_ms": round(lin, 5),
+           "linear_tops": round(ops / lin / 1e9, 2), "rotq_ms": round(rq, 5),
+           "rotq_gbs": round((layer.M * layer.K * 3 + layer.M * 4 + layer.K) / rq / 1e6, 1),
+           "weight_copies": len(sets)}
+    del sets, x
+    torch.cuda.empty_cache()
+    return layer, out
+
+
+def section_decode(torch, twl, steps, warmup):
+    import workloads as W
+    res = {}
+    for name in ("decode_gate_up", "decode_down"):
+        layer = W.make_config(name)
+        x_full, sign, sets = upload_layer(torch, twl, layer, n_copies(layer.N, layer.K))
+        per_m = {}
+        for M in W.DECODE_MS:
+            x = x_full[:M].contiguous()
+            timer = Timer(torch)
+            ms = run_layer_steps(torch, twl, x, sign, sets, steps, warmup, timer)
+            lin = timer.mean_ms("linear")
+            wb = weight_bytes(layer.N, layer.K)
+            tot = wb + M * layer.K + M * 4 + 4 * M * layer.N
+            per_m[str(M)] = {"ms_per_step": round(ms, 5), "linear_ms": round(lin, 5),
+                             "weight_gbs": round(wb / lin / 1e6, 1),
+                             "hbm_frac": round(wb / lin / 1e6 / PEAK_HBM_GBS, 4),
+                             "total_gbs": round(tot / lin / 1e6, 1),
+                             "valu_frac": round(2.0 * M * layer.N * layer.K / lin / 1e9 / PEAK_VALU_DOT4_TOPS, 4),
+                             "rotq_ms": round(timer.mean_ms("rotq"), 5)}
+        res[name] = {"K": layer.K, "N": layer.N, "by_M": per_m}
+        del sets, x_full
+        torch.cuda.empty_cache()
+    return res
+
+
+def section_stack(torch, twl, steps, warmup):
+    """64 decoder layers x {proj 5120->5120, gate_up 5120->34816, down 17408->5120}."""
+    import workloads as W
+    signs = {k: torch.from_numpy(v).cuda() for k, v in W.stack_signs().items()}
+    layers = []
+    for L in range(W.N_LAYERS):
+        lin = []
+        for which in range(3):
+            xb, code, s = W.stack_linear_torch(L, which, 512, "cuda")
+            packed, q, smax = twl.pack_ternary(code, s)
+            del code
+            lin.append((xb, packed, q, smax))
+        layers.append(lin)
+    torch.cuda.synchronize()
+    out = {}
+    for M in (512, 24):
+        bufs = {}
+        for which, (_, K, N, _, _) in enumerate(W.STACK_LINEARS):
+            bufs[which] = (torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                           torch.empty((M,), dtype=torch.float32, device="cuda"),
+                           torch.empty((M, N), dtype=torch.float32, device="cuda"),
+                           torch.zeros(max(1, twl.workspace_bytes(M, N, K)), dtype=torch.uint8, device="cuda"))
+        xs = [[lin[w][0][:M].contiguous() for w in range(3)] for lin in layers]
+
+        def step():
+            for L, lin in enumerate(layers):
+                for which, (_, packed, q, smax) in enumerate(lin):
+                    K = W.STACK_LINEARS[which][1]
+                    x_i8, a_scale, y, ws = bufs[which]
+                    twl.rotate_quant_act(xs[L][which], signs[K], out=(x_i8, a_scale))
+                    twl.ternary_linear(x_i8, a_scale, packed, q, smax, out=y, workspace=ws)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        ops = 2.0 * M * sum(N * K for _, K, N, _, _ in W.STACK_LINEARS) * W.N_LAYERS
+        wb = sum(weight_bytes(N, K) for _, K, N, _, _ in W.STACK_LINEARS) * W.N_LAYERS
+        out["prefill_M512" if M == 512 else "decode_M24"] = {
+            "ms_per_step": round(ms, 4), "tops": round(ops / ms / 1e9, 2),
+            "weight_gbs": round(wb / ms / 1e6, 1), "launches": 6 * W.N_LAYERS}
+        del xs, bufs
+    del layers
+    torch.cuda.empty_cache()
+    return out
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description="ternary linear layer benchmark (one MI355X)")
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sections", default=",".join(SECTIONS),
+                    help="comma list of: " + ", ".join(SECTIONS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (no collectives, no sharding); "
+              "run it with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import ternary_weight_linear_block_amd as twl
+    twl.library()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    sections = [s for s in args.sections.split(",") if s]
+    detail = {"device": torch.cuda.get_device_name(0)}
+
+    log("headline: prefill gate/up M=512 K=5120 N=17408")
+    layer, head = section_layer(torch, twl, "prefill_gate_up", args.steps, args.warmup)
+    detail["prefill_gate_up"] = head
+    if "down" in sections:
+        log("prefill down M=256 K=17408 N=5120")
+        detail["prefill_down"] = section_layer(torch, twl, "prefill_down", args.steps, args.warmup)[1]
+    if "decode" in sections:
+        log("decode sweep")
+        detail["decode"] = section_decode(torch, twl, args.steps, args.warmup)
+    if "stack" in sections:
+        log("64-layer stack")
+        detail["stack"] = section_stack(torch, twl, max(2, args.steps // 10), 1)
+
+    ops = 2.0 * layer.M * layer.N * layer.K
+    achieved = ops / head["linear_ms"] / 1e9
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
+                "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                "traffic": traffic_for("gemm_i8.hip", "prefill_gate_up"),
+                "kernel": "gemm_kernel (ternary_linear GEMM path)",
+                "algorithmic_ops_per_launch": ops}
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(layer)
+
+    rec = {"metric": METRIC, "value": head["step_tops"], "unit": "TOPS", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+           "data": "synthetic",
+           "config": {"workload": "prefill_gate_up", "M": layer.M, "K": layer.K, "N": layer.N,
+                      "step": "rotate_quant_act + ternary_linear", "parallelism": "none (1 GPU)"},
+           "roofline": roofline, "cpu_baseline": cpu, "detail": detail}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,149 @@
+/*
+ * twl.h -- C ABI of the MI355X (gfx950) ternary linear layer library.
+ *
+ * The operation (pages cited by title and section):
+ *   [P1] "Ternary-Bonsai-2-27B on 2x RTX 5070 with vLLM TP=2"
+ *        (qiita.com/nakanokensetsu/items/ecc183fae033565af7cb)
+ *        Prerequisites -- weights are {-1,0,+1} in 2 bits with one scale per
+ *          128 elements; a block-wise Hadamard rotation sits on the input side.
+ *        Section 1 -- the rotation's sign table is keyed by the full input
+ *          width; H1024 [a; b] = [H512 a + H512 b ; H512 a - H512 b].
+ *        Section 4 (prefill linear layers to an int8 GEMM) -- s[n,g] is split
+ *          as q[n,g] = round(127 s[n,g] / smax[n]); W_int8 = code * q fits int8;
+ *          the matmul becomes one int8 GEMM with int32 accumulation plus a
+ *          per-row and per-token rescale; activations are quantised to int8
+ *          per token after the rotation.
+ *        Section 5 (what did not help) -- a dp4a decode GEMV.
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers on the current HIP device, owned
+ *     by the caller, contiguous and row-major, at least 16-byte aligned.  The
+ *     library allocates nothing and keeps no per-call state.
+ *   - Work is enqueued on `stream` (NULL = the legacy default stream) and is
+ *     asynchronous; nothing synchronises.  Outputs are valid once the stream
+ *     reaches that point.
+ *   - Shape, null-pointer and alignment errors are detected on the host before
+ *     anything is enqueued and return a non-zero status; twl_last_error() then
+ *     holds a message (thread-local).  A failed launch returns TWL_EHIP.
+ *     Faults inside kernels surface at the caller's next synchronisation.
+ *   - K must be a positive multiple of 1024 (whole Hadamard blocks) and at
+ *     most TWL_MAX_K; M and N may be any value >= 0 (0 enqueues nothing).
+ *   - Non-finite activations or scales give unspecified results.
+ */
+#ifndef TWL_H
+#define TWL_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TWL_OK = 0,
+  TWL_EINVAL = 1,   /* null pointer, negative size, bad enum value        */
+  TWL_ESHAPE = 2,   /* K not a multiple of 1024, K > TWL_MAX_K, too large  */
+  TWL_EALIGN = 3,   /* a pointer is not 16-byte aligned                    */
+  TWL_EDEVICE = 4,  /* the current device is not gfx950                   */
+  TWL_EHIP = 5      /* a HIP runtime call or kernel launch failed          */
+} twl_status;
+
+#define TWL_HBLOCK 1024      /* Hadamard block width along K              */
+#define TWL_GROUP 128        /* K elements per weight scale group         */
+#define TWL_MAX_K 65536      /* 64 blocks; |acc| <= 127*127*K < 2^31       */
+#define TWL_GEMV_MAX_M 24    /* decode batches up to this size use the GEMV */
+
+/* Which kernel family computes the linear layer (twl_ternary_linear_ex). */
+typedef enum {
+  TWL_PATH_AUTO = 0,     /* GEMV for M <= TWL_GEMV_MAX_M, else the MFMA GEMM */
+  TWL_PATH_GEMM = 1,     /* int8-MFMA GEMM with in-register 2-bit unpack     */
+  TWL_PATH_GEMV = 2      /* packed-2-bit dot4 GEMV (M <= TWL_GEMV_MAX_M)     */
+} twl_path;
+
+/*
+ * rotate_quant_act -- [P1] Prerequisites, section 1 and section 4.
+ *   For every token t and 1024-block b:
+ *     r[t, 1024b:1024b+1024] = (1/32) * H1024 * (sign[1024b:...] * x[t, ...])
+ *   with H1024 the Sylvester Hadamard matrix, evaluated as an fp32 fast
+ *   Walsh-Hadamard transform with stages h = 1, 2, ..., 512 (each butterfly
+ *   (lo, hi) -> (lo + hi, lo - hi)).  Then, per token over the whole row:
+ *     a_scale[t] = max_k |r[t,k]| / 127              (fp32, IEEE division)
+ *     x_i8[t,k]  = clamp(rint(r[t,k] / a_scale[t]), -127, 127)  (ties to even)
+ *   An all-zero token gives a_scale = 0 and x_i8 = 0.
+ *   x       in : bf16 bit patterns [M, K]
+ *   sign    in : int8 [K], each +1 or -1 (one table per input width)
+ *   x_i8    out: int8 [M, K]
+ *   a_scale out: fp32 [M]
+ */
+twl_status twl_rotate_quant_act(const uint16_t* x, const int8_t* sign, int64_t M, int64_t K,
+                                int8_t* x_i8, float* a_scale, hipStream_t stream);
+
+/*
+ * pack_ternary -- [P1] Prerequisites and section 4 (load time, once per weight).
+ *   smax[n]  = max_g |s[n,g]|                               (fp32, exact)
+ *   q[n,g]   = rint((127 * s[n,g]) / smax[n])  in fp32, ties to even; 0 if smax = 0
+ *   packed   : 2 bits per code, u = code + 1 in {0,1,2}; row n is K/16
+ *              little-endian 32-bit words and code k = 16w + 4i + b lives in
+ *              bits [8b + 2i, 8b + 2i + 1] of word w (four codes per byte).
+ *   code      in : int8 [N, K], values in {-1, 0, +1}
+ *   s         in : fp16 bit patterns [N, K/128]
+ *   packed    out: uint8 [N, K/4]
+ *   q         out: int8 [N, K/128], |q| <= 127
+ *   smax      out: fp32 [N]
+ *   bad_codes out: optional (may be NULL) device int32 counter; the number of
+ *              codes outside {-1,0,+1} is ADDED to it.  Such codes pack as 0.
+ */
+twl_status twl_pack_ternary(const int8_t* code, const uint16_t* s, int64_t N, int64_t K,
+                            uint8_t* packed, int8_t* q, float* smax, int32_t* bad_codes,
+                            hipStream_t stream);
+
+/* Bytes of workspace twl_ternary_linear* needs for this shape (0 = none). */
+size_t twl_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * ternary_linear -- [P1] section 4 (prefill GEMM) and section 5 (decode GEMV).
+ *   acc[t,n] = sum_k x_i8[t,k] * code[n,k] * q[n, k/128]      (exact int32)
+ *   y[t,n]   = acc[t,n] * a_scale[t] * smax[n] / 127           (fp32)
+ *   Prefill sizes run an int8-MFMA GEMM that unpacks the 2-bit codes on chip;
+ *   decode batches (M <= TWL_GEMV_MAX_M) run a packed-2-bit GEMV.  Both give
+ *   bit-identical acc.
+ *   x_i8 [M,K], a_scale [M], packed [N,K/4], q [N,K/128], smax [N] as produced
+ *   by the two calls above; y out: fp32 [M, N].
+ *   workspace: device memory of at least twl_workspace_bytes(M,N,K) bytes; may
+ *   be NULL when that is 0.
+ */
+twl_status twl_ternary_linear(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
+                              const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
+                              float* y, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ternary_linear_acc -- the same kernels with the rescale left out: writes the
+ * exact int32 accumulators acc [M, N] (for bit-exact verification).
+ */
+twl_status twl_ternary_linear_acc(const int8_t* x_i8, const uint8_t* packed, const int8_t* q,
+                                  int64_t M, int64_t N, int64_t K, int32_t* acc,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ternary_linear_ex -- explicit kernel family.  out_acc != 0 writes int32 acc
+ * into `out` (a_scale and smax are then ignored and may be NULL), otherwise fp32
+ * y.  TWL_PATH_GEMV requires M <= TWL_GEMV_MAX_M.
+ */
+twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
+                                 const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
+                                 void* out, int out_acc, int path,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* twl_last_error(void);
+
+/* ABI version of this header (bumped on incompatible changes). */
+int twl_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TWL_H */

@@ -1,0 +1,132 @@
+"""Ternary linear layer for MI355X (gfx950): Python binding of libtwl.so.
+
+Three operations, each one call into the C ABI declared in include/twl.h
+(argument marshalling only; every step runs in the library's HIP kernels):
+
+  rotate_quant_act(x, sign)              -> (x_i8, a_scale)
+  pack_ternary(code, s)                  -> (packed, q, smax)
+  ternary_linear(x_i8, a_scale, packed, q, smax) -> y
+
+PyTorch provides device memory and the current stream.  Tensors must be CUDA
+(HIP) tensors on the current device, contiguous; x is bf16 (or its int16 bit
+pattern), s is fp16 (or int16 bits), code and sign are int8.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+from . import _lib
+from ._lib import GEMV_MAX_M, GROUP, HBLOCK, MAX_K, PATH_AUTO, PATH_GEMM, PATH_GEMV, TwlError
+
+__all__ = [
+    "rotate_quant_act", "pack_ternary", "ternary_linear", "ternary_linear_acc",
+    "workspace_bytes", "TwlError", "PATH_AUTO", "PATH_GEMM", "PATH_GEMV", "GEMV_MAX_M",
+    "HBLOCK", "GROUP", "MAX_K", "library",
+]
+
+
+def library():
+    """The loaded ctypes library (raises ImportError if it is not built)."""
+    return _lib.load()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream=None) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dev_ptr(t, name: str, dtypes) -> int:
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def rotate_quant_act(x, sign, out: Optional[Tuple] = None, stream=None):
+    """x [M, K] bf16, sign [K] int8 -> (x_i8 [M, K] int8, a_scale [M] fp32)."""
+    torch = _torch()
+    lib = _lib.load()
+    M, K = x.shape
+    if out is None:
+        x_i8 = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        a_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    else:
+        x_i8, a_scale = out
+    st = lib.twl_rotate_quant_act(
+        _dev_ptr(x, "x", (torch.bfloat16, torch.int16)), _dev_ptr(sign, "sign", (torch.int8,)),
+        M, K, _dev_ptr(x_i8, "x_i8", (torch.int8,)), _dev_ptr(a_scale, "a_scale", (torch.float32,)),
+        _stream_handle(stream))
+    _lib.check(st, "twl_rotate_quant_act")
+    return x_i8, a_scale
+
+
+def pack_ternary(code, s, bad_codes=None, stream=None):
+    """code [N, K] int8, s [N, K/128] fp16 -> (packed [N, K/4] uint8, q [N, K/128] int8, smax [N] fp32)."""
+    torch = _torch()
+    lib = _lib.load()
+    N, K = code.shape
+    packed = torch.empty((N, K // 4), dtype=torch.uint8, device=code.device)
+    q = torch.empty((N, K // GROUP), dtype=torch.int8, device=code.device)
+    smax = torch.empty((N,), dtype=torch.float32, device=code.device)
+    bad = 0 if bad_codes is None else _dev_ptr(bad_codes, "bad_codes", (torch.int32,))
+    st = lib.twl_pack_ternary(
+        _dev_ptr(code, "code", (torch.int8,)), _dev_ptr(s, "s", (torch.float16, torch.int16)), N, K,
+        _dev_ptr(packed, "packed", (torch.uint8,)), _dev_ptr(q, "q", (torch.int8,)),
+        _dev_ptr(smax, "smax", (torch.float32,)), bad or None, _stream_handle(stream))
+    _lib.check(st, "twl_pack_ternary")
+    return packed, q, smax
+
+
+def workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(_lib.load().twl_workspace_bytes(M, N, K))
+
+
+def _linear(x_i8, a_scale, packed, q, smax, out_acc: bool, path: int, out=None, workspace=None,
+            stream=None):
+    torch = _torch()
+    lib = _lib.load()
+    M, K = x_i8.shape
+    N = packed.shape[0]
+    if packed.shape[1] * 4 != K:
+        raise ValueError(f"packed has {packed.shape[1]} bytes per row, expected K/4 = {K // 4}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.int32 if out_acc else torch.float32, device=x_i8.device)
+    need = workspace_bytes(M, N, K)
+    ws_ptr, ws_len = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=x_i8.device)
+        ws_ptr, ws_len = _dev_ptr(workspace, "workspace", (torch.uint8,)), workspace.numel()
+    st = lib.twl_ternary_linear_ex(
+        _dev_ptr(x_i8, "x_i8", (torch.int8,)),
+        None if out_acc else _dev_ptr(a_scale, "a_scale", (torch.float32,)),
+        _dev_ptr(packed, "packed", (torch.uint8,)), _dev_ptr(q, "q", (torch.int8,)),
+        None if out_acc else _dev_ptr(smax, "smax", (torch.float32,)),
+        M, N, K, _dev_ptr(out, "out", (torch.int32,) if out_acc else (torch.float32,)),
+        1 if out_acc else 0, path, ws_ptr, ws_len, _stream_handle(stream))
+    _lib.check(st, "twl_ternary_linear_ex")
+    return out
+
+
+def ternary_linear(x_i8, a_scale, packed, q, smax, path: int = PATH_AUTO, out=None,
+                   workspace=None, stream=None):
+    """y [M, N] fp32 = (sum_k x_i8 * code * q) * a_scale[t] * smax[n] / 127."""
+    return _linear(x_i8, a_scale, packed, q, smax, False, path, out, workspace, stream)
+
+
+def ternary_linear_acc(x_i8, packed, q, path: int = PATH_AUTO, out=None, workspace=None,
+                       stream=None):
+    """The exact int32 accumulators acc [M, N] of the same kernels (no rescale)."""
+    return _linear(x_i8, None, packed, q, None, True, path, out, workspace, stream)

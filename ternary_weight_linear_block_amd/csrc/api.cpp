@@ -1,0 +1,202 @@
+// C ABI of the ternary linear library: argument validation, device checks,
+// GEMM/GEMV dispatch and thread-local error messages.  No allocation, no
+// synchronisation; every kernel is enqueued on the caller's stream.
+#include "twl.h"
+#include "twl_internal.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+twl_status fail(twl_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+twl_status ok() {
+  g_last_error.clear();
+  return TWL_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+bool g_dev_known[kMaxDevices];
+bool g_dev_ok[kMaxDevices];
+twl::DeviceInfo g_dev_info[kMaxDevices];
+
+// Checks the current device is gfx950 and returns its cached facts.
+twl_status current_device(twl::DeviceInfo* out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TWL_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TWL_EDEVICE, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  if (!g_dev_known[dev]) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(TWL_EHIP, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+    g_dev_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    g_dev_info[dev].cu_count = prop.multiProcessorCount;
+    g_dev_known[dev] = true;
+    if (!g_dev_ok[dev])
+      return fail(TWL_EDEVICE, "device %d is %s; this library is built for gfx950 only", dev,
+                  prop.gcnArchName);
+  }
+  if (!g_dev_ok[dev]) return fail(TWL_EDEVICE, "device %d is not gfx950", dev);
+  *out = g_dev_info[dev];
+  return TWL_OK;
+}
+
+twl_status check_k(int64_t K) {
+  if (K <= 0 || K % TWL_HBLOCK != 0)
+    return fail(TWL_ESHAPE, "K=%lld must be a positive multiple of %d", static_cast<long long>(K),
+                TWL_HBLOCK);
+  if (K > TWL_MAX_K)
+    return fail(TWL_ESHAPE, "K=%lld exceeds the maximum %d", static_cast<long long>(K), TWL_MAX_K);
+  return TWL_OK;
+}
+
+twl_status check_rows(const char* name, int64_t v) {
+  if (v < 0) return fail(TWL_EINVAL, "%s=%lld is negative", name, static_cast<long long>(v));
+  if (v > (int64_t{1} << 30))
+    return fail(TWL_ESHAPE, "%s=%lld is too large", name, static_cast<long long>(v));
+  return TWL_OK;
+}
+
+#define TWL_REQUIRE_PTR(p)                                                 \
+  do {                                                                     \
+    if ((p) == nullptr) return fail(TWL_EINVAL, "%s is NULL", #p);          \
+    if (!aligned16(p)) return fail(TWL_EALIGN, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+#define TWL_TRY(expr)                    \
+  do {                                   \
+    twl_status st_ = (expr);             \
+    if (st_ != TWL_OK) return st_;       \
+  } while (0)
+
+twl_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(TWL_EHIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* twl_last_error(void) { return g_last_error.c_str(); }
+
+int twl_abi_version(void) { return 1; }
+
+twl_status twl_rotate_quant_act(const uint16_t* x, const int8_t* sign, int64_t M, int64_t K,
+                                int8_t* x_i8, float* a_scale, hipStream_t stream) {
+  TWL_TRY(check_rows("M", M));
+  TWL_TRY(check_k(K));
+  if (M == 0) return ok();
+  TWL_REQUIRE_PTR(x);
+  TWL_REQUIRE_PTR(sign);
+  TWL_REQUIRE_PTR(x_i8);
+  TWL_REQUIRE_PTR(a_scale);
+  twl::DeviceInfo dev;
+  TWL_TRY(current_device(&dev));
+  return launched(twl::launch_rotate_quant(x, sign, M, K, x_i8, a_scale, stream),
+                  "rotate_quant_act");
+}
+
+twl_status twl_pack_ternary(const int8_t* code, const uint16_t* s, int64_t N, int64_t K,
+                            uint8_t* packed, int8_t* q, float* smax, int32_t* bad_codes,
+                            hipStream_t stream) {
+  TWL_TRY(check_rows("N", N));
+  TWL_TRY(check_k(K));
+  if (N == 0) return ok();
+  TWL_REQUIRE_PTR(code);
+  TWL_REQUIRE_PTR(s);
+  TWL_REQUIRE_PTR(packed);
+  TWL_REQUIRE_PTR(q);
+  TWL_REQUIRE_PTR(smax);
+  if (bad_codes != nullptr && (reinterpret_cast<uintptr_t>(bad_codes) & 3u))
+    return fail(TWL_EALIGN, "bad_codes is not 4-byte aligned");
+  twl::DeviceInfo dev;
+  TWL_TRY(current_device(&dev));
+  return launched(twl::launch_pack(code, s, N, K, packed, q, smax, bad_codes, stream),
+                  "pack_ternary");
+}
+
+size_t twl_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  twl::DeviceInfo dev;
+  if (current_device(&dev) != TWL_OK) return 0;
+  if (M <= TWL_GEMV_MAX_M) return 0;
+  return twl::gemm_workspace_bytes(M, N, K, dev);
+}
+
+twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
+                                 const int8_t* q, const float* smax, int64_t M, int64_t N,
+                                 int64_t K, void* out, int out_acc, int path, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  TWL_TRY(check_rows("M", M));
+  TWL_TRY(check_rows("N", N));
+  TWL_TRY(check_k(K));
+  if (path != TWL_PATH_AUTO && path != TWL_PATH_GEMM && path != TWL_PATH_GEMV)
+    return fail(TWL_EINVAL, "unknown path %d", path);
+  if (path == TWL_PATH_GEMV && M > TWL_GEMV_MAX_M)
+    return fail(TWL_ESHAPE, "the GEMV path takes M <= %d (got %lld)", TWL_GEMV_MAX_M,
+                static_cast<long long>(M));
+  if (M == 0 || N == 0) return ok();
+  TWL_REQUIRE_PTR(x_i8);
+  TWL_REQUIRE_PTR(packed);
+  TWL_REQUIRE_PTR(q);
+  TWL_REQUIRE_PTR(out);
+  if (!out_acc) {
+    TWL_REQUIRE_PTR(a_scale);
+    TWL_REQUIRE_PTR(smax);
+  }
+  twl::DeviceInfo dev;
+  TWL_TRY(current_device(&dev));
+  const bool use_gemv = path == TWL_PATH_GEMV || (path == TWL_PATH_AUTO && M <= TWL_GEMV_MAX_M);
+  if (use_gemv)
+    return launched(twl::launch_gemv(x_i8, a_scale, packed, q, smax, M, N, K, out, out_acc != 0,
+                                     dev, stream),
+                    "ternary_linear (GEMV)");
+  const size_t need = twl::gemm_workspace_bytes(M, N, K, dev);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(TWL_EINVAL, "workspace of %zu bytes required (got %zu)", need,
+                  workspace == nullptr ? size_t{0} : workspace_bytes);
+    if (!aligned16(workspace)) return fail(TWL_EALIGN, "workspace is not 16-byte aligned");
+  }
+  return launched(twl::launch_gemm(x_i8, a_scale, packed, q, smax, M, N, K, out, out_acc != 0,
+                                   workspace, workspace_bytes, dev, stream),
+                  "ternary_linear (GEMM)");
+}
+
+twl_status twl_ternary_linear(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
+                              const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
+                              float* y, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  return twl_ternary_linear_ex(x_i8, a_scale, packed, q, smax, M, N, K, y, 0, TWL_PATH_AUTO,
+                               workspace, workspace_bytes, stream);
+}
+
+twl_status twl_ternary_linear_acc(const int8_t* x_i8, const uint8_t* packed, const int8_t* q,
+                                  int64_t M, int64_t N, int64_t K, int32_t* acc, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  return twl_ternary_linear_ex(x_i8, nullptr, packed, q, nullptr, M, N, K, acc, 1, TWL_PATH_AUTO,
+                               workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

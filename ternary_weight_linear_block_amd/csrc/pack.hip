@@ -1,0 +1,109 @@
+// pack_ternary: load-time conversion of {-1,0,+1} codes and fp16 group scales
+// into the library's weight format.
+//
+// Method ([P1] "Ternary-Bonsai-2-27B on 2x RTX 5070 with vLLM TP=2",
+// Prerequisites and section 4): each row n has an fp16 scale s[n,g] per
+// 128-element group; it is split into the row maximum smax[n] and an 8-bit
+// ratio q[n,g] = round(127 s[n,g] / smax[n]) so that code * q fits int8.
+// Here smax = max_g |s| kept exactly in fp32, 127*s is exact in fp32 (an
+// 11-bit significand times a 7-bit integer), one correctly rounded fp32
+// division follows and rintf rounds ties to even.
+//
+// 2-bit format (this library's choice; the pages fix only "2 bits per code"):
+// u = code + 1 in {0, 1, 2}; row n is K/16 little-endian 32-bit words and code
+// k = 16w + 4i + b sits in bits [8b + 2i, 8b + 2i + 1] of word w.  With this
+// interleave one shift and one AND turn a word into four bytes holding u for
+// four consecutive k, which the GEMM and GEMV consume directly.
+//
+// One workgroup per row: the scale reduction, the q row and the packed row are
+// produced together.  The pass is HBM bound (K + K/4 + K/64 bytes per row).
+#include "twl_internal.h"
+
+namespace twl {
+namespace {
+
+__device__ __forceinline__ float fp16_bits_to_float(uint16_t bits) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, bits));
+}
+
+__global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ code,
+                                                   const uint16_t* __restrict__ s, int K,
+                                                   uint8_t* __restrict__ packed,
+                                                   int8_t* __restrict__ q,
+                                                   float* __restrict__ smax,
+                                                   int32_t* __restrict__ bad_codes) {
+  const int n = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int G = K >> 7;
+  const uint16_t* sr = s + static_cast<size_t>(n) * G;
+
+  // smax[n] = max_g |s[n,g]|
+  float m = 0.0f;
+  for (int g = tid; g < G; g += 256) m = fmaxf(m, fabsf(fp16_bits_to_float(sr[g])));
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) m = fmaxf(m, __shfl_xor(m, sh));
+  __shared__ float wmax[4];
+  __shared__ int wbad[4];
+  if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  __syncthreads();
+  const float rmax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  if (tid == 0) smax[n] = rmax;
+
+  // q[n,g] = rint(fl32(127 s) / smax), 0 for an all-zero row
+  int8_t* qr = q + static_cast<size_t>(n) * G;
+  for (int g = tid; g < G; g += 256) {
+    float r = 0.0f;
+    if (rmax > 0.0f) r = rintf((127.0f * fp16_bits_to_float(sr[g])) / rmax);
+    qr[g] = static_cast<int8_t>(static_cast<int>(r));
+  }
+
+  // 2-bit packing, one 16-code word per thread iteration
+  const int8_t* cr = code + static_cast<size_t>(n) * K;
+  uint32_t* pr = reinterpret_cast<uint32_t*>(packed + static_cast<size_t>(n) * (K >> 2));
+  int nbad = 0;
+  for (int w = tid; w < (K >> 4); w += 256) {
+    const uint4 c = *reinterpret_cast<const uint4*>(cr + 16 * w);
+    const uint32_t d[4] = {c.x, c.y, c.z, c.w};
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t di = d[i];  // bytes: codes k = 16w + 4i + b, b = 0..3
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t byte = (di >> (8 * b)) & 0xFFu;
+        if (!(byte == 0x00u || byte == 0x01u || byte == 0xFFu)) {
+          ++nbad;
+          di &= ~(0xFFu << (8 * b));  // an invalid code packs as 0
+        }
+      }
+      // per byte: 0xFF -> 0, 0x00 -> 1, 0x01 -> 2, without carries between bytes
+      const uint32_t u = ((di & 0x7F7F7F7Fu) + 0x01010101u) & 0x03030303u;
+      word |= u << (2 * i);
+    }
+    pr[w] = word;
+  }
+
+  if (bad_codes != nullptr) {
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) nbad += __shfl_xor(nbad, sh);
+    if ((tid & 63) == 0) wbad[tid >> 6] = nbad;
+    __syncthreads();
+    if (tid == 0) {
+      const int total = wbad[0] + wbad[1] + wbad[2] + wbad[3];
+      if (total) atomicAdd(bad_codes, total);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack(const int8_t* code, const uint16_t* s, int64_t N, int64_t K,
+                       uint8_t* packed, int8_t* q, float* smax, int32_t* bad_codes,
+                       hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>(N)), dim3(256), 0, stream, code, s,
+                     static_cast<int>(K), packed, q, smax, bad_codes);
+  return hipGetLastError();
+}
+
+}  // namespace twl

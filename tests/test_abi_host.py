@@ -1,0 +1,91 @@
+"""Host-side checks of the C ABI that need no GPU: the built library loads,
+exports every function include/twl.h declares, and rejects bad arguments on
+the host (shape, null pointer, alignment) before touching the device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "twl.h")
+
+twl = pytest.importorskip("ternary_weight_linear_block_amd")
+from ternary_weight_linear_block_amd import _lib  # noqa: E402
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(twl_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libtwl.so is not built; run `python -m ternary_weight_linear_block_amd.build`")
+    return _lib.load()
+
+
+def test_header_declares_the_three_operations():
+    names = _declared_functions()
+    for n in ("twl_rotate_quant_act", "twl_pack_ternary", "twl_ternary_linear"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert names
+    for n in names:
+        assert hasattr(lib, n), n
+    # the binding's prototypes cover exactly the header's functions
+    assert sorted(s[0] for s in _lib.SIGNATURES) == names
+
+
+def test_abi_version(lib):
+    assert lib.twl_abi_version() == 1
+
+
+FAKE = 0x10000   # 16-byte aligned, never dereferenced: every call below fails host validation
+
+
+@pytest.mark.parametrize("K", [0, 1000, 1024 + 128, 65536 + 1024])
+def test_rotate_rejects_bad_k(lib, K):
+    st = lib.twl_rotate_quant_act(FAKE, FAKE, 4, K, FAKE, FAKE, None)
+    assert st == 2  # TWL_ESHAPE
+    assert b"K=" in lib.twl_last_error()
+
+
+def test_rotate_rejects_null_and_misaligned(lib):
+    assert lib.twl_rotate_quant_act(None, FAKE, 4, 1024, FAKE, FAKE, None) == 1
+    assert b"x is NULL" in lib.twl_last_error()
+    assert lib.twl_rotate_quant_act(FAKE + 2, FAKE, 4, 1024, FAKE, FAKE, None) == 3
+    assert lib.twl_rotate_quant_act(FAKE, FAKE, -1, 1024, FAKE, FAKE, None) == 1
+
+
+def test_pack_rejects_bad_args(lib):
+    assert lib.twl_pack_ternary(FAKE, FAKE, 8, 1000, FAKE, FAKE, FAKE, None, None) == 2
+    assert lib.twl_pack_ternary(FAKE, None, 8, 1024, FAKE, FAKE, FAKE, None, None) == 1
+    assert lib.twl_pack_ternary(FAKE, FAKE, 8, 1024, FAKE, FAKE, FAKE, FAKE + 2, None) == 3
+
+
+def test_linear_rejects_bad_args(lib):
+    ex = lib.twl_ternary_linear_ex
+    # unknown path
+    assert ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 1024, FAKE, 0, 7, None, 0, None) == 1
+    # GEMV path beyond its batch limit
+    assert ex(FAKE, FAKE, FAKE, FAKE, FAKE, 25, 4, 1024, FAKE, 0, 2, None, 0, None) == 2
+    # y output needs a_scale and smax; acc output does not
+    assert ex(FAKE, None, FAKE, FAKE, FAKE, 4, 4, 1024, FAKE, 0, 0, None, 0, None) == 1
+    assert ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 3072 + 64, FAKE, 1, 0, None, 0, None) == 2
+    assert lib.twl_ternary_linear(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 1024, FAKE + 8, None, 0, None) == 3
+
+
+def test_empty_shapes_enqueue_nothing(lib):
+    # M = 0 or N = 0 return OK before any device query
+    assert lib.twl_rotate_quant_act(None, None, 0, 1024, None, None, None) == 0
+    assert lib.twl_pack_ternary(None, None, 0, 1024, None, None, None, None, None) == 0
+    assert lib.twl_ternary_linear(None, None, None, None, None, 0, 5, 1024, None, None, 0, None) == 0
+    assert lib.twl_ternary_linear(None, None, None, None, None, 5, 0, 1024, None, None, 0, None) == 0
+    assert lib.twl_last_error() == b""

@@ -1,0 +1,231 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on the
+same seeded inputs.  Bit-exact for x_i8, a_scale, packed, q, smax and the int32
+accumulators; fp32 y within 1e-5 relative, element by element.
+"""
+import numpy as np
+import pytest
+
+import oracle.twl_oracle as O
+import workloads as W
+from tests.gpu_helpers import announce, dev, gpu_linear, gpu_pack, gpu_rotq, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+Y_RTOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def twl():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ternary_weight_linear_block_amd as m
+    m.library()  # raises if libtwl.so is missing: no fallback exists
+    return m
+
+
+def _oracle_layer(layer):
+    x_i8, a_scale = O.rotate_quant_act(layer.x_bits, layer.sign)
+    packed, q, smax = O.pack_ternary(layer.code, layer.s_bits)
+    return x_i8, a_scale, packed, q, smax
+
+
+def _check_rotq(twl, x_bits, sign, label):
+    announce(f"rotate_quant_act {label} M={x_bits.shape[0]} K={x_bits.shape[1]}")
+    gx, gs = gpu_rotq(twl, x_bits, sign)
+    ox, os_ = O.rotate_quant_act(x_bits, sign)
+    assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32)), f"{label}: a_scale differs"
+    bad = np.argwhere(gx != ox)
+    assert bad.size == 0, f"{label}: {len(bad)} x_i8 mismatches, first {bad[:5].tolist()}"
+    return ox, os_
+
+
+def _check_pack(twl, code, s_bits, label):
+    announce(f"pack_ternary {label} N={code.shape[0]} K={code.shape[1]}")
+    packed, q, smax = gpu_pack(twl, code, s_bits)
+    op, oq, osm = O.pack_ternary(code, s_bits)
+    assert np.array_equal(host(packed), op), f"{label}: packed differs"
+    assert np.array_equal(host(q), oq), f"{label}: q differs"
+    assert np.array_equal(host(smax).view(np.uint32), osm.view(np.uint32)), f"{label}: smax differs"
+    return packed, q, smax, oq, osm
+
+
+def _check_linear(twl, x_i8, a_scale, packed, q, smax, code, oq, osm, path, label):
+    pname = {0: "auto", 1: "gemm", 2: "gemv"}[path]
+    M, N = x_i8.shape[0], code.shape[0]
+    announce(f"ternary_linear_acc {label} path={pname} M={M} N={N} K={x_i8.shape[1]}")
+    acc = gpu_linear(twl, x_i8, a_scale, packed, q, smax, path, True)
+    oacc = O.linear_acc(x_i8, code, oq)
+    bad = np.argwhere(acc != oacc)
+    assert bad.size == 0, f"{label}/{pname}: {len(bad)} acc mismatches, first {bad[:5].tolist()}"
+    announce(f"ternary_linear {label} path={pname}")
+    y = gpu_linear(twl, x_i8, a_scale, packed, q, smax, path, False)
+    np.testing.assert_allclose(y, O.epilogue(oacc, a_scale, osm), rtol=Y_RTOL, atol=0)
+    return acc, y
+
+
+# ----------------------------------------------------------- the five configs
+
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_rotate_quant_act_configs(twl, name):
+    layer = W.make_config(name)
+    _check_rotq(twl, layer.x_bits, layer.sign, name)
+
+
+def test_config_tiny_end_to_end_both_paths(twl):
+    layer = W.make_config("tiny")
+    x_i8, a_scale = _check_rotq(twl, layer.x_bits, layer.sign, "tiny")
+    packed, q, smax, oq, osm = _check_pack(twl, layer.code, layer.s_bits, "tiny")
+    acc_gemm, _ = _check_linear(twl, x_i8, a_scale, packed, q, smax, layer.code, oq, osm, 1, "tiny")
+    acc_gemv, _ = _check_linear(twl, x_i8, a_scale, packed, q, smax, layer.code, oq, osm, 2, "tiny")
+    assert np.array_equal(acc_gemm, acc_gemv)
+    # sanity against the unquantised float64 product ([P1] section 4: ~9.5e-3)
+    y = gpu_linear(twl, x_i8, a_scale, packed, q, smax, 0, False)
+    e = O.rel_err(y, O.float_reference(layer.x_bits, layer.sign, layer.code, layer.s_bits))
+    assert 3e-3 < e < 2.5e-2, e
+
+
+@pytest.mark.parametrize("name", ["prefill_gate_up", "prefill_down"])
+def test_prefill_configs_full(twl, name):
+    layer = W.make_config(name)
+    x_i8, a_scale = _check_rotq(twl, layer.x_bits, layer.sign, name)
+    packed, q, smax, oq, osm = _check_pack(twl, layer.code, layer.s_bits, name)
+    _check_linear(twl, x_i8, a_scale, packed, q, smax, layer.code, oq, osm, 0, name)
+
+
+@pytest.mark.parametrize("name", ["decode_gate_up", "decode_down"])
+def test_decode_sweep_full(twl, name):
+    layer = W.make_config(name)
+    packed, q, smax, oq, osm = _check_pack(twl, layer.code, layer.s_bits, name)
+    for M in W.DECODE_MS:
+        xb = np.ascontiguousarray(layer.x_bits[:M])
+        x_i8, a_scale = _check_rotq(twl, xb, layer.sign, f"{name} M={M}")
+        _check_linear(twl, x_i8, a_scale, packed, q, smax, layer.code, oq, osm, 0, f"{name} M={M}")
+
+
+def test_stack_sampled_layers(twl):
+    """64-layer stack: three layers spread over the stack, each of the three
+    linears, prefill M=512 and decode M=24, inputs drawn on the GPU; the oracle
+    checks rotation/quantisation in full and the linear on sampled outputs."""
+    signs = W.stack_signs()
+    rng = np.random.default_rng(99)
+    for layer in (0, 37, 63):
+        for which in range(3):
+            name, K, N, _, _ = W.STACK_LINEARS[which]
+            x_bits_d, code_d, s_bits_d = W.stack_linear_torch(layer, which, 512, "cuda")
+            code_h = host(code_d)
+            s_h = host(s_bits_d).view(np.uint16)
+            lbl0 = f"stack L{layer} {name}"
+            announce(f"pack_ternary {lbl0} N={N} K={K}")
+            packed, q, smax = twl.pack_ternary(code_d, s_bits_d)
+            oq, osm = O.decompose_scales(s_h)
+            assert np.array_equal(host(q), oq), lbl0
+            assert np.array_equal(host(smax).view(np.uint32), osm.view(np.uint32)), lbl0
+            prow = rng.integers(0, N, 64)
+            assert np.array_equal(host(packed)[prow], O.pack_codes(code_h[prow])), lbl0
+            xb = host(x_bits_d).view(np.uint16)
+            for M in (512, 24):
+                lbl = f"stack L{layer} {name} M={M}"
+                x_i8, a_scale = _check_rotq(twl, np.ascontiguousarray(xb[:M]), signs[K], lbl)
+                announce(f"ternary_linear {lbl}")
+                acc = gpu_linear(twl, x_i8, a_scale, packed, q, smax, 0, True)
+                y = gpu_linear(twl, x_i8, a_scale, packed, q, smax, 0, False)
+                rows = rng.integers(0, M, 256)
+                cols = rng.integers(0, N, 256)
+                oacc = O.linear_acc_at(x_i8, code_h, oq, rows, cols)
+                assert np.array_equal(acc[rows, cols], oacc), lbl
+                np.testing.assert_allclose(y[rows, cols], O.epilogue_at(oacc, a_scale, osm, rows, cols),
+                                           rtol=Y_RTOL, atol=0)
+            del code_d, code_h
+
+
+# ------------------------------------------------ tiles, ragged tails, edges
+
+@pytest.mark.parametrize("M,N,K", [(300, 200, 2048), (25, 513, 1024), (64, 64, 1024),
+                                   (257, 257, 3072), (512, 1024, 1024), (129, 96, 4096)])
+def test_gemm_ragged_shapes(twl, M, N, K):
+    layer = W.make_layer(1000 + M + N, M, K, N, codes="sparse40")
+    x_i8, a_scale = _check_rotq(twl, layer.x_bits, layer.sign, "ragged")
+    packed, q, smax, oq, osm = _check_pack(twl, layer.code, layer.s_bits, "ragged")
+    _check_linear(twl, x_i8, a_scale, packed, q, smax, layer.code, oq, osm, 1, f"ragged {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 13, 17, 24])
+@pytest.mark.parametrize("N,K", [(1, 1024), (65, 2048), (1000, 5120)])
+def test_gemv_vs_gemm_shapes(twl, M, N, K):
+    layer = W.make_layer(2000 + M * 7 + N, M, K, N)
+    x_i8, a_scale = O.rotate_quant_act(layer.x_bits, layer.sign)
+    packed, q, smax, oq, osm = _check_pack(twl, layer.code, layer.s_bits, "gemv")
+    a1, _ = _check_linear(twl, x_i8, a_scale, packed, q, smax, layer.code, oq, osm, 2, f"gemv M={M}")
+    a2, _ = _check_linear(twl, x_i8, a_scale, packed, q, smax, layer.code, oq, osm, 1, f"gemm M={M}")
+    assert np.array_equal(a1, a2)
+
+
+def test_rotate_edge_cases(twl):
+    # maximum width (64 blocks), one token
+    layer = W.make_layer(31, 2, 65536, 1)
+    _check_rotq(twl, layer.x_bits, layer.sign, "K=65536")
+    # a zero token and a single-spike token
+    x = np.zeros((3, 2048), dtype=np.uint16)
+    x[1, 7] = W.f32_to_bf16_bits(np.array([3.0], dtype=np.float32))[0]
+    x[2] = W.f32_to_bf16_bits(np.linspace(-4, 4, 2048, dtype=np.float32))
+    sign = np.where(np.arange(2048) % 3 == 0, -1, 1).astype(np.int8)
+    gx, gs = _check_rotq(twl, x, sign, "zero/spike")
+    assert gs[0] == 0 and not gx[0].any()
+    # 17 blocks (odd count, two blocks per wave)
+    layer = W.make_layer(32, 5, 17408, 1, act="silu_gate")
+    _check_rotq(twl, layer.x_bits, layer.sign, "K=17408")
+
+
+def test_pack_edge_cases(twl):
+    # an all-zero scale row, a negative scale, and invalid codes
+    code = np.random.default_rng(3).integers(-1, 2, size=(4, 1024)).astype(np.int8)
+    s = np.full((4, 8), 0.01, dtype=np.float16)
+    s[1] = 0
+    s[2, 3] = -0.02
+    _check_pack(twl, code, s.view(np.uint16), "zero/negative scales")
+    bad_code = code.copy()
+    bad_code[3, 5] = 2
+    bad_code[3, 900] = -7
+    counter = torch.zeros(1, dtype=torch.int32, device="cuda")
+    packed, _, _ = gpu_pack(twl, bad_code, s.view(np.uint16), bad=counter)
+    assert int(host(counter)[0]) == 2
+    fixed = bad_code.copy()
+    fixed[3, 5] = 0
+    fixed[3, 900] = 0
+    assert np.array_equal(host(packed), O.pack_codes(fixed))
+
+
+def test_empty_inputs(twl):
+    x = torch.empty((0, 1024), dtype=torch.int16, device="cuda")
+    sign = torch.ones(1024, dtype=torch.int8, device="cuda")
+    xi, sc = twl.rotate_quant_act(x, sign)
+    assert xi.shape == (0, 1024)
+    layer = W.make_layer(5, 1, 1024, 8)
+    packed, q, smax = gpu_pack(twl, layer.code, layer.s_bits)
+    y = twl.ternary_linear(torch.empty((0, 1024), dtype=torch.int8, device="cuda"),
+                           torch.empty(0, device="cuda"), packed, q, smax)
+    assert y.shape == (0, 8)
+
+
+def test_shape_errors_enqueue_nothing(twl):
+    x = torch.zeros((4, 1000), dtype=torch.int16, device="cuda")
+    sign = torch.ones(1000, dtype=torch.int8, device="cuda")
+    with pytest.raises(twl.TwlError) as e:
+        twl.rotate_quant_act(x, sign)
+    assert e.value.status == 2
+
+
+def test_repeat_runs_are_bitwise_identical(twl):
+    layer = W.make_config("prefill_down")
+    x = dev(layer.x_bits.view(np.int16))
+    sign = dev(layer.sign)
+    packed, q, smax = gpu_pack(twl, layer.code, layer.s_bits)
+    outs = []
+    for _ in range(2):
+        announce("repeat prefill_down")
+        xi, sc = twl.rotate_quant_act(x, sign)
+        outs.append((host(xi), host(twl.ternary_linear(xi, sc, packed, q, smax))))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
