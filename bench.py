@@ -52,32 +52,6 @@ def weight_bytes(N: int, K: int) -> int:
     return N * K // 4 + N * K // 128 + 4 * N
 
 
-class Timer:
-    """HIP-event timing of individual launches on torch's current stream."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = {}
-
-    def __call__(self, key, fn):
-        ev0 = self.torch.cuda.Event(enable_timing=True)
-        ev1 = self.torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        out = fn()
-        ev1.record()
-        self.pairs.setdefault(key, []).append((ev0, ev1))
-        return out
-
-    def mean_ms(self, key):
-        ps = self.pairs.get(key, [])
-        if not ps:
-            return None
-        return sum(a.elapsed_time(b) for a, b in ps) / len(ps)
-
-    def reset(self):
-        self.pairs = {}
-
-
 def upload_layer(torch, twl, layer, copies: int):
     """Host layer -> device x, sign and `copies` packed weight sets."""
     x = torch.from_numpy(layer.x_bits.view("int16")).cuda()
@@ -96,8 +70,14 @@ def n_copies(N: int, K: int) -> int:
     return max(1, -(-CACHE_BUST_BYTES // weight_bytes(N, K)))
 
 
-def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, timer):
-    """warmup + timed steps of rotate_quant_act + ternary_linear; returns ms/step."""
+def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, kernel_iters=50):
+    """warmup + timed steps of rotate_quant_act + ternary_linear.
+
+    Returns (ms per step from the wall clock around exactly `steps` steps,
+    mean ms of one rotate_quant_act launch, mean ms of one ternary_linear
+    launch); the per-kernel means come from HIP events around back-to-back
+    launches of that kernel alone on the current stream (weights cycled).
+    """
     M, K = x.shape
     N = sets[0][0].shape[0]
     x_i8 = torch.empty((M, K), dtype=torch.int8, device="cuda")
@@ -106,24 +86,34 @@ def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, timer):
     ws_n = twl.workspace_bytes(M, N, K)
     ws = torch.zeros(max(ws_n, 1), dtype=torch.uint8, device="cuda")
 
-    def step(i, timed):
+    def rotq():
+        twl.rotate_quant_act(x, sign, out=(x_i8, a_scale))
+
+    def linear(i):
         packed, q, smax = sets[i % len(sets)]
-        if timed:
-            timer("rotq", lambda: twl.rotate_quant_act(x, sign, out=(x_i8, a_scale)))
-            timer("linear", lambda: twl.ternary_linear(x_i8, a_scale, packed, q, smax, out=y,
-                                                        workspace=ws))
-        else:
-            twl.rotate_quant_act(x, sign, out=(x_i8, a_scale))
-            twl.ternary_linear(x_i8, a_scale, packed, q, smax, out=y, workspace=ws)
+        twl.ternary_linear(x_i8, a_scale, packed, q, smax, out=y, workspace=ws)
 
     for i in range(warmup):
-        step(i, False)
+        rotq()
+        linear(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i, True)
+        rotq()
+        linear(i)
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    for _ in range(kernel_iters):
+        rotq()
+    ev[1].record()
+    for i in range(kernel_iters):
+        linear(i)
+    ev[2].record()
+    torch.cuda.synchronize()
+    return ms_step, ev[0].elapsed_time(ev[1]) / kernel_iters, ev[1].elapsed_time(ev[2]) / kernel_iters
 
 
 def traffic_for(kernel_src: str, workload: str):
@@ -173,10 +163,7 @@ def section_layer(torch, twl, name, steps, warmup):
     import workloads as W
     layer = W.make_config(name)
     x, sign, sets = upload_layer(torch, twl, layer, n_copies(layer.N, layer.K))
-    timer = Timer(torch)
-    ms = run_layer_steps(torch, twl, x, sign, sets, steps, warmup, timer)
-    lin = timer.mean_ms("linear")
-    rq = timer.mean_ms("rotq")
+    ms, rq, lin = run_layer_steps(torch, twl, x, sign, sets, steps, warmup)
     ops = 2.0 * layer.M * layer.N * layer.K
     out = {"M": layer.M, "K": layer.K, "N": layer.N, "ms_per_step": round(ms, 5),
            "step_tops": round(ops / ms / 1e9, 2), "linear_ms": round(lin, 5),
@@ -197,9 +184,7 @@ def section_decode(torch, twl, steps, warmup):
         per_m = {}
         for M in W.DECODE_MS:
             x = x_full[:M].contiguous()
-            timer = Timer(torch)
-            ms = run_layer_steps(torch, twl, x, sign, sets, steps, warmup, timer)
-            lin = timer.mean_ms("linear")
+            ms, rq, lin = run_layer_steps(torch, twl, x, sign, sets, steps, warmup)
             wb = weight_bytes(layer.N, layer.K)
             tot = wb + M * layer.K + M * 4 + 4 * M * layer.N
             per_m[str(M)] = {"ms_per_step": round(ms, 5), "linear_ms": round(lin, 5),
@@ -207,7 +192,7 @@ def section_decode(torch, twl, steps, warmup):
                              "hbm_frac": round(wb / lin / 1e6 / PEAK_HBM_GBS, 4),
                              "total_gbs": round(tot / lin / 1e6, 1),
                              "valu_frac": round(2.0 * M * layer.N * layer.K / lin / 1e9 / PEAK_VALU_DOT4_TOPS, 4),
-                             "rotq_ms": round(timer.mean_ms("rotq"), 5)}
+                             "rotq_ms": round(rq, 5)}
         res[name] = {"K": layer.K, "N": layer.N, "by_M": per_m}
         del sets, x_full
         torch.cuda.empty_cache()

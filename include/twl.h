@@ -84,9 +84,10 @@ twl_status twl_rotate_quant_act(const uint16_t* x, const int8_t* sign, int64_t M
  * pack_ternary -- [P1] Prerequisites and section 4 (load time, once per weight).
  *   smax[n]  = max_g |s[n,g]|                               (fp32, exact)
  *   q[n,g]   = rint((127 * s[n,g]) / smax[n])  in fp32, ties to even; 0 if smax = 0
- *   packed   : 2 bits per code, u = code + 1 in {0,1,2}; row n is K/16
- *              little-endian 32-bit words and code k = 16w + 4i + b lives in
- *              bits [8b + 2i, 8b + 2i + 1] of word w (four codes per byte).
+ *   packed   : 2 bits per code, field u = 0 for -1, 1 for +1, 2 for 0; row n
+ *              is K/16 little-endian 32-bit words and code k = 16w + 4i + b
+ *              lives in bits [8b + 2i, 8b + 2i + 1] of word w (four codes per
+ *              byte).
  *   code      in : int8 [N, K], values in {-1, 0, +1}
  *   s         in : fp16 bit patterns [N, K/128]
  *   packed    out: uint8 [N, K/4]
@@ -99,7 +100,12 @@ twl_status twl_pack_ternary(const int8_t* code, const uint16_t* s, int64_t N, in
                             uint8_t* packed, int8_t* q, float* smax, int32_t* bad_codes,
                             hipStream_t stream);
 
-/* Bytes of workspace twl_ternary_linear* needs for this shape (0 = none). */
+/*
+ * Bytes of workspace twl_ternary_linear* may need for this shape on the
+ * current device (0 = none; valid for every path).  The workspace holds the
+ * GEMM's split-K partial tiles; its contents on entry do not matter (no
+ * clearing needed) and calls sharing a workspace must not run concurrently.
+ */
 size_t twl_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*

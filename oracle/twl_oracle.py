@@ -33,10 +33,11 @@ Readings taken where the pages are silent (each is listed in the design notes):
   x_i8 = rint(r / a_scale) (IEEE division, ties to even);  R7 "round" is ties to
   even;  R8 q is evaluated as rint(fl32(127 s) / smax) in fp32, smax = max_g |s|
   stored exactly as fp32;  R9 an all-zero token gives a_scale = 0, x_i8 = 0, an
-  all-zero scale row gives smax = 0, q = 0;  R10 2-bit encoding u = code + 1,
-  sixteen codes per little-endian 32-bit word, code k = 16w + 4i + b in bits
-  [8b + 2i, 8b + 2i + 1] of word w;  R11 the epilogue y = acc * a_scale[t] *
-  smax[n] / 127 is evaluated in float64 and rounded to fp32 once.
+  all-zero scale row gives smax = 0, q = 0;  R10 2-bit encoding u = 0 for -1,
+  1 for +1, 2 for 0 (3 unused), sixteen codes per little-endian 32-bit word,
+  code k = 16w + 4i + b in bits [8b + 2i, 8b + 2i + 1] of word w;  R11 the
+  epilogue y = acc * a_scale[t] * smax[n] / 127 is evaluated in float64 and
+  rounded to fp32 once.
 """
 from __future__ import annotations
 
@@ -132,6 +133,11 @@ def decompose_scales(s_bits: np.ndarray):
     return q.astype(np.int8), smax
 
 
+# R10: the 2-bit field value of each code, and its inverse
+CODE_TO_FIELD = {-1: 0, 1: 1, 0: 2}
+FIELD_TO_CODE = {v: k for k, v in CODE_TO_FIELD.items()}
+
+
 def pack_codes(code: np.ndarray) -> np.ndarray:
     """{-1,0,+1} codes [N, K] -> packed bytes [N, K/4] in the R10 layout."""
     code = np.asarray(code)
@@ -140,7 +146,11 @@ def pack_codes(code: np.ndarray) -> np.ndarray:
         raise ValueError("K must be a multiple of 16")
     if np.any((code < -1) | (code > 1)):
         raise ValueError("codes must be in {-1, 0, +1}")
-    u = (code.astype(np.int64) + 1).reshape(N, K // 16, 4, 4)   # [n, w, i, b]
+    c = code.astype(np.int64)
+    u = np.zeros_like(c)
+    for cv, fv in CODE_TO_FIELD.items():
+        u[c == cv] = fv
+    u = u.reshape(N, K // 16, 4, 4)                                 # [n, w, i, b]
     words = np.zeros((N, K // 16), dtype=np.uint64)
     for i in range(4):
         for b in range(4):
@@ -157,7 +167,13 @@ def unpack_codes(packed: np.ndarray, K: int) -> np.ndarray:
     for i in range(4):
         for b in range(4):
             u[:, :, i, b] = ((words >> np.uint64(8 * b + 2 * i)) & np.uint64(3)).astype(np.int64)
-    return (u.reshape(N, K) - 1).astype(np.int8)
+    u = u.reshape(N, K)
+    if np.any(u == 3):
+        raise ValueError("field value 3 does not encode a code")
+    code = np.zeros((N, K), dtype=np.int8)
+    for fv, cv in FIELD_TO_CODE.items():
+        code[u == fv] = cv
+    return code
 
 
 def pack_ternary(code: np.ndarray, s_bits: np.ndarray):

@@ -32,8 +32,12 @@ COMMON_FLAGS = [
     "-fPIC",
     "-std=c++17",
     "-ffp-contract=off",
+    # keep MFMA accumulators in arch VGPRs: the AGPR form makes LLVM reshuffle
+    # loop-carried accumulators with v_accvgpr copies every iteration
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall",
     "-Wno-unused-command-line-argument",
+    "-Wno-inline-asm",  # the GEMM names M0 as clobbered on purpose (see gemm_i8.hip)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE,
     "-I", CSRC,

@@ -140,7 +140,7 @@ size_t twl_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   twl::DeviceInfo dev;
   if (current_device(&dev) != TWL_OK) return 0;
-  if (M <= TWL_GEMV_MAX_M) return 0;
+  // the GEMM's need, also for M <= TWL_GEMV_MAX_M (TWL_PATH_GEMM may be forced)
   return twl::gemm_workspace_bytes(M, N, K, dev);
 }
 

@@ -10,28 +10,49 @@
 // The pages expand W_int8 in a separate pass every step (section 6 timing
 // table: 31 of 83 ms) before a library int8 GEMM.  Here W_int8 never exists in
 // memory: each lane turns one packed 32-bit word (16 codes) into the 16 int8
-// bytes of its MFMA B operand with 3 shifts, 4 ANDs and 4 byte-permutes
-// against the table {-q, 0, +q}.
+// bytes of its MFMA B operand with 1 shift, 4 ANDs and 4 byte-permutes
+// against tables built from {-q, +q, 0}.
 //
 // gfx950 mapping
-//   * v_mfma_i32_32x32x32_i8: a 32x32 output tile, K = 32 per instruction;
-//     each lane supplies 16 bytes of A (one row) and 16 bytes of B (one
-//     column).  Integer accumulation is exact, so the assignment of k values
-//     to (lane half, byte) only has to be the same for A and B: lane half h
-//     at k-step s of a 128-group covers k = 16 (4h + s) .. +15, which makes a
-//     lane's B data for a whole group one 16-byte load of packed words.
-//   * Workgroup: 4 waves in a 2x2 grid, wave tile (32 RM) x (32 RN), block
-//     tile (64 RM) x (64 RN).  The x_i8 tile of a group (BM x 128 bytes) is
-//     staged in LDS, double buffered, with a 16-byte-chunk XOR swizzle so the
-//     column-wise ds_read_b128 of the A operand hits distinct banks.
-//   * Packed weights go from global memory straight to registers (prefetched
-//     one group ahead); they are 1/4 of an int8 operand, so a second LDS
-//     round trip would cost more than it saves.
-//   * Epilogue: acc -> fp32 with a_scale[row] and smax[col]/127, stored row
-//     major (32 consecutive floats per half-wave).
+//   * v_mfma_i32_32x32x32_i8 (measured full rate on gfx950: 32 cycles per
+//     32x32x32; the 16x16x64 form is markedly slower per MAC).  Each lane
+//     supplies 16 bytes of A (one row) and 16 bytes of B (one column) per
+//     instruction.  Integer accumulation is exact, so the k values assigned to
+//     (lane half h, byte) only have to agree between A and B: in a 128-k
+//     pipeline stage (one scale group), lane half h at k-step s covers
+//     k = 16 (4 h + s) .. +15, so a lane's B data for a whole stage is 16
+//     contiguous packed bytes (4 words) and its scale is q[n, g].
+//   * Workgroup: 8 waves, two per SIMD.  Block tile BM = 64 RM rows x
+//     BN = 32 FN columns split 2 along M x 2 along N; wave (wm, wn) owns RM row
+//     fragments and ceil(FN/2) column fragments (an odd FN leaves wn=1 one
+//     padding fragment), and the two waves (wk = 0, 1) of each (wm, wn) take
+//     k-steps {0,1} and {2,3} of every stage.  The pair's int32 partials are
+//     added through LDS at the end (exact).  Two waves per SIMD let one wave's
+//     unpack VALU and LDS reads run while the other's MFMAs execute; with one
+//     wave per SIMD these costs were measured to add up.
+//   * Multi-stage pipeline (4 stages; 3 for 256-row tiles) of direct
+//     global->LDS loads (global_load_lds dwordx4: no VGPR staging).  A stage
+//     holds BM x 128 bytes of x_i8 (8 lanes per row; 16-byte chunks
+//     XOR-swizzled by row so the column-wise ds_read_b128 hits distinct banks)
+//     and BN x 32 bytes of packed weights (2 lanes per weight row, the two
+//     16-byte halves parity-swizzled by column).  Each load instruction thus
+//     touches few cache lines; the q block of the tile is copied to LDS once
+//     up front.  Every wave issues the same static set of loads per stage,
+//     waits only for its own (vmcnt), and a bare s_barrier publishes the
+//     stage.  No load into VGPRs happens inside the loop, so the compiler
+//     never has to drain vmcnt.
+//   * Optional split-K over stages: each split stores its exact int32 partial
+//     tile (lane-major, fully coalesced) to a workspace slot and a second,
+//     small kernel adds the splits and runs the epilogue.  (A device-scope
+//     fence + counter scheme in one kernel was measured to cost far more: on
+//     this multi-XCD part each fence writes back the L2.)
+//   * Tiles are ordered so that the workgroups sharing a column block (the
+//     same weights) land on the same XCD and its L2.
 #include "twl_internal.h"
 
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 
 namespace twl {
 namespace {
@@ -39,62 +60,283 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
+constexpr int kStages = 4;       // pipeline depth
+constexpr int kStageK = 128;     // k per stage = one scale group
+constexpr int kXcds = 8;         // MI355X: 8 XCDs, workgroups dispatched round robin
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] + vmcnt_hi[15:14], expcnt[6:4], lgkmcnt[11:8]
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without the memory fence __syncthreads implies: LDS
+// visibility is established by each wave's explicit vmcnt wait before it.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct global->LDS loads (lane i writes LDS[lds_base + i * size]) at
+// address sbase (wave-uniform, SGPR pair) + voff (per lane, 32 bit).  Issued
+// as inline asm on purpose: the compiler then does not see these LDS writes
+// and does not drain vmcnt before every LDS read of the other stages; the
+// kernel orders them itself (wait_vmcnt on its own loads + bare_barrier).
+// M0 is set inside the same statement; the compiler does not use M0 in this
+// kernel (checked by a test on the generated code).
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory", "m0");
+}
+
+// LDS byte offset of a __shared__ object (generic -> local address space).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)(p)));
+}
+
 // 16-byte chunk swizzle inside a 128-byte LDS row: distinct chunks for any 8
 // consecutive rows (32-bank view) and for the even / odd rows of any 16
 // consecutive rows (64-bank view).
 __device__ __forceinline__ int chunk_swizzle(int row) { return (row ^ (row >> 3)) & 7; }
 
-// Four int8 bytes {code * q} for the 2-bit fields at bit offset `shift` of
-// each byte of `word` (u = 0, 1, 2 selects byte 0, 1, 2 of `table`).
-__device__ __forceinline__ int unpack4(uint32_t word, int shift, uint32_t table) {
-  const uint32_t sel = (word >> shift) & 0x03030303u;
-  return static_cast<int>(__builtin_amdgcn_perm(0u, table, sel));
+// The 16 int8 weights {code * q} of one packed word (16 codes), as the four
+// dwords of an MFMA / dot4 operand (dword i = codes 4i .. 4i+3 of the word).
+// Fields at bits 0-1 / 4-5 of each byte are selectors {0,1,2} into
+// ta = [-q, +q, 0, 0]; fields at bits 2-3 / 6-7, masked in place, are
+// selectors {0,4,8}: byte 0 of tb1 (-q), byte 0 of tb0 (+q), or the sign fill
+// of tb1's byte 1, which is 0.  9 VALU operations per 16 codes.
+struct QTables {
+  uint32_t ta, tb0, tb1;
+};
+
+__device__ __forceinline__ QTables make_tables(int qv) {
+  const uint32_t neg = static_cast<uint32_t>(-qv) & 0xFFu;
+  const uint32_t pos = static_cast<uint32_t>(qv) & 0xFFu;
+  return QTables{neg | (pos << 8), pos, neg};
 }
 
-template <int RM, int RN, bool OUT_ACC>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(
-    const int8_t* __restrict__ x, const float* __restrict__ a_scale,
-    const uint8_t* __restrict__ packed, const int8_t* __restrict__ q,
-    const float* __restrict__ smax, int M, int N, int K, void* __restrict__ out) {
-  constexpr int BM = 64 * RM;
-  constexpr int BN = 64 * RN;
-  constexpr int A_LOADS = BM * 8 / 256;  // 16-byte chunks per thread per group
-  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * 128];
+__device__ __forceinline__ v4i unpack16(uint32_t w, const QTables& t) {
+  const uint32_t w4 = w >> 4;
+  v4i b;
+  b.x = static_cast<int>(__builtin_amdgcn_perm(0u, t.ta, w & 0x03030303u));
+  b.y = static_cast<int>(__builtin_amdgcn_perm(t.tb0, t.tb1, w & 0x0C0C0C0Cu));
+  b.z = static_cast<int>(__builtin_amdgcn_perm(0u, t.ta, w4 & 0x03030303u));
+  b.w = static_cast<int>(__builtin_amdgcn_perm(t.tb0, t.tb1, w4 & 0x0C0C0C0Cu));
+  return b;
+}
+
+constexpr int kQTileBytes = 16384;  // q of a block tile: BN columns x its groups
+
+template <int RM, int FN>
+struct Tile {
+  static constexpr int RN = (FN + 1) / 2;      // column fragments per wave
+  static constexpr int BM = 64 * RM;
+  static constexpr int BN = 32 * FN;
+  static constexpr int STAGES = RM >= 4 ? 3 : kStages;
+  static constexpr int A_BYTES = BM * kStageK; // x_i8 of one stage
+  static constexpr int B_BYTES = BN * 32;      // BN columns x 2 half-planes x 16 B
+  static constexpr int A_INSTR = A_BYTES / 1024;   // 1 KB per load instruction
+  static constexpr int B_INSTR = B_BYTES / 1024;
+  static constexpr int A_PER_WAVE = (A_INSTR + 7) / 8;
+  static constexpr int B_PER_WAVE = (B_INSTR + 7) / 8;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int LOADS_PER_STAGE = A_PER_WAVE + B_PER_WAVE;
+  static constexpr int SLOT_INTS = 4 * RM * RN * 64 * 16;  // one split's partial tile
+  // wave-pair reduction: fragments exchanged per round through the LDS
+  static constexpr int XCH_FRAGS = LDS_BYTES / (4 * 4096);
+  static_assert(XCH_FRAGS >= 1, "LDS too small for the wave-pair exchange");
+  static_assert(2 * LOADS_PER_STAGE < 64, "vmcnt range");
+};
+
+struct GemmArgs {
+  const int8_t* x;
+  const float* a_scale;
+  const uint8_t* packed;
+  const int8_t* q;
+  const float* smax;
+  void* out;
+  int32_t* ws_part;    // [tiles][splits][SLOT_INTS] split-K partial tiles
+  int M, N, K;
+  int tiles_m, tiles_n, splits, stages_per_split;
+};
+
+// Writes one wave's RM x RN fragments of the output tile: fp32 y with the
+// per-row / per-column scales (staged in LDS) or the raw int32 accumulators.
+// 32x32 accumulator layout: lane holds column l32 of a fragment; register r
+// holds row 8 (r / 4) + 4 half + (r % 4).
+template <int RM, int FN, bool OUT_ACC>
+__device__ __forceinline__ void store_tile(const v16i (&acc)[RM][(FN + 1) / 2], void* out,
+                                           const float* row_scale, const float* col_scale,
+                                           int M, int N, int m0, int n0, int wm, int wn,
+                                           int lane) {
+  constexpr int RN = (FN + 1) / 2;
+  const int l32 = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < RN; ++j) {
+    const int f = wn * RN + j;
+    if (f >= FN) continue;  // padding fragment
+    const int cl = 32 * f + l32;
+    const int col = n0 + cl;
+    if (col >= N) continue;
+    const float cscale = OUT_ACC ? 0.0f : col_scale[cl];
+#pragma unroll
+    for (int i = 0; i < RM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = wm * 32 * RM + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int row = m0 + rl;
+        if (row < M) {
+          const size_t o = static_cast<size_t>(row) * N + col;
+          if (OUT_ACC)
+            static_cast<int32_t*>(out)[o] = acc[i][j][r];
+          else
+            static_cast<float*>(out)[o] = static_cast<float>(acc[i][j][r]) * row_scale[rl] * cscale;
+        }
+      }
+    }
+  }
+}
+
+// Work item of a workgroup: XCD-aware order (consecutive items share a column
+// block, i.e. the same weights, and land on one XCD), then (column block, row
+// block, split).
+struct WorkItem {
+  int tile, split, m0, n0;
+};
+
+__device__ __forceinline__ WorkItem work_item(int bid, int tiles_m, int tiles_n, int splits,
+                                              int bm, int bn) {
+  const int total = tiles_m * tiles_n * splits;
+  const int per = total / kXcds, rem = total % kXcds;
+  const int xcd = bid % kXcds;
+  const int lin = xcd * per + min(xcd, rem) + bid / kXcds;
+  WorkItem w;
+  w.split = lin % splits;
+  w.tile = lin / splits;
+  w.m0 = (w.tile % tiles_m) * bm;
+  w.n0 = (w.tile / tiles_m) * bn;
+  return w;
+}
+
+template <int RM, int FN, bool OUT_ACC>
+__global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs p) {
+  using T = Tile<RM, FN>;
+  constexpr int RN = T::RN, BN = T::BN;
+  __shared__ __attribute__((aligned(1024))) int8_t smem[T::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) int8_t q_lds[kQTileBytes];
+  // epilogue scales of this tile, staged once: a_scale of its rows and
+  // smax / 127 of its columns (reading them from global memory next to the
+  // output stores would order every load behind the stores before it)
+  __shared__ float row_scale[T::BM];
+  __shared__ float col_scale[T::BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1;
-  const int wn = wave >> 1;
-  const int half = lane >> 5;
+  const int wn = (wave >> 1) & 1;
+  const int wk = wave >> 2;  // which two k-steps of each stage
   const int l32 = lane & 31;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
-  const int G = K >> 7;
-  const size_t KB = static_cast<size_t>(K) >> 2;
+  const int half = lane >> 5;
 
-  // Global -> LDS assignment for the A tile: chunk c = tid + 256 p covers row
-  // c / 8, 16-byte chunk c % 8 (8 lanes read one 128-byte row segment).
-  const int8_t* a_src[A_LOADS];
-  int a_dst[A_LOADS];
+  const WorkItem w = work_item(blockIdx.x, p.tiles_m, p.tiles_n, p.splits, T::BM, BN);
+  const int m0 = w.m0, n0 = w.n0;
+  const int M = p.M, N = p.N, K = p.K;
+  const size_t KB = static_cast<size_t>(K) >> 2;
+  const int G = K >> 7;
+  const int st_begin = w.split * p.stages_per_split;
+  const int st_end = min(G, st_begin + p.stages_per_split);
+
+  // ---- once per tile: scales, and the q block [BN columns] x [groups g0 ..
+  // g0 + qw) (qw a multiple of 4; rows of q are contiguous, so this is a
+  // coalesced dword copy).  The planner keeps BN * qw <= kQTileBytes.
+  const int g0 = st_begin & ~3;
+  const int qw = (st_end - g0 + 3) & ~3;
+  {
+    const int qd = qw >> 2;
+    for (int idx = tid; idx < BN * qd; idx += 512) {
+      const int c = idx / qd, d = idx - c * qd;
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(
+          p.q + static_cast<size_t>(min(n0 + c, N - 1)) * G + g0 + 4 * d);
+      *reinterpret_cast<uint32_t*>(q_lds + c * qw + 4 * d) = v;
+    }
+    if (!OUT_ACC) {
+      for (int r = tid; r < T::BM; r += 512) row_scale[r] = p.a_scale[min(m0 + r, M - 1)];
+      for (int c = tid; c < BN; c += 512) col_scale[c] = p.smax[min(n0 + c, N - 1)] * (1.0f / 127.0f);
+    }
+  }
+  __syncthreads();
+
+  // ---- this wave's direct-to-LDS load slots.  Global addresses are a
+  // wave-uniform tile base (SGPRs) plus a 32-bit per-lane offset; rows and
+  // columns past M / N are clamped to the last one (computed, never stored).
+  // Load instructions are dealt round robin to the 8 waves; every wave issues
+  // the same number per stage (a wave past the last instruction of a kind
+  // repeats an earlier one: same data to the same LDS bytes), which keeps the
+  // per-stage load count static for the vmcnt bookkeeping.
+  const int8_t* x_tile = p.x + static_cast<size_t>(m0) * K;
+  const uint8_t* w_tile = p.packed + static_cast<size_t>(n0) * KB;
+  // A: instruction ia covers rows 8 ia .. 8 ia + 7 (1 KB, 8 lanes per 128-byte
+  // row); lane -> row, 16-B slot, holding chunk slot ^ swizzle(row)
+  uint32_t a_off[T::A_PER_WAVE];
+  int a_lds[T::A_PER_WAVE];
 #pragma unroll
-  for (int p = 0; p < A_LOADS; ++p) {
-    const int c = tid + 256 * p;
-    const int row = c >> 3;
-    const int ch = c & 7;
-    const int grow = min(m0 + row, M - 1);  // rows past M are computed, never stored
-    a_src[p] = x + static_cast<size_t>(grow) * K + ch * 16;
-    a_dst[p] = row * 128 + ((ch ^ chunk_swizzle(row)) << 4);
+  for (int i = 0; i < T::A_PER_WAVE; ++i) {
+    const int ia = (wave + 8 * i) % T::A_INSTR;
+    const int r = 8 * ia + (lane >> 3);
+    const int chunk = (lane & 7) ^ chunk_swizzle(r);
+    a_off[i] = static_cast<uint32_t>((min(m0 + r, M - 1) - m0) * K + 16 * chunk);
+    a_lds[i] = ia * 1024;
+  }
+  // B: instruction ib covers columns 32 ib .. 32 ib + 31 (2 lanes per column:
+  // its 32 bytes of the stage); LDS slot 2 col + p holds half-plane
+  // h = p ^ ((col >> 3) & 1), which spreads a fragment read over all banks.
+  uint32_t b_off[T::B_PER_WAVE];
+  int b_lds[T::B_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < T::B_PER_WAVE; ++i) {
+    const int ib = (wave + 8 * i) % T::B_INSTR;
+    const int col = 32 * ib + (lane >> 1);
+    const int h = (lane & 1) ^ ((col >> 3) & 1);
+    b_off[i] = static_cast<uint32_t>((min(n0 + col, N - 1) - n0) * KB + 16 * h);
+    b_lds[i] = T::A_BYTES + ib * 1024;
   }
 
-  // B operand rows (weight rows = output columns) of this lane.
-  const uint8_t* b_src[RN];
-  const int8_t* q_src[RN];
+  const uint32_t smem_base = lds_addr(smem);
+  // load instruction `i` (A first, then B) of stage `st` into buffer `buf`
+  auto issue_one = [&](int i, int st, int buf) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(smem_base + buf * T::STAGE_BYTES);
+    if (i < T::A_PER_WAVE)
+      dma16(x_tile + static_cast<size_t>(st) * kStageK, a_off[i], base + a_lds[i]);
+    else
+      dma16(w_tile + static_cast<size_t>(st) * (kStageK / 4), b_off[i - T::A_PER_WAVE],
+            base + b_lds[i - T::A_PER_WAVE]);
+  };
+  auto issue = [&](int st, int buf) {
+#pragma unroll
+    for (int i = 0; i < T::LOADS_PER_STAGE; ++i) issue_one(i, st, buf);
+  };
+
+  // ---- operand fragments of this lane
+  int a_row[RM];
+#pragma unroll
+  for (int i = 0; i < RM; ++i) a_row[i] = wm * 32 * RM + 32 * i + l32;
+  int b_slot[RN];  // LDS byte offset of this lane's B data in a stage
+  int q_pos[RN];   // offset of this lane's column in the q block
 #pragma unroll
   for (int j = 0; j < RN; ++j) {
-    const int n = min(n0 + wn * 32 * RN + 32 * j + l32, N - 1);
-    b_src[j] = packed + static_cast<size_t>(n) * KB + half * 16;
-    q_src[j] = q + static_cast<size_t>(n) * G;
+    const int c = min(32 * (wn * RN + j) + l32, BN - 1);  // padding fragment clamped
+    b_slot[j] = (2 * c + (half ^ ((c >> 3) & 1))) * 16 + 8 * wk;
+    q_pos[j] = c * qw - g0;
   }
 
   v16i acc[RM][RN];
@@ -103,165 +345,292 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(
 #pragma unroll
     for (int j = 0; j < RN; ++j) acc[i][j] = v16i{0};
 
-  uint4 bcur[RN];
-  int qcur[RN];
-  uint4 astage[A_LOADS];
+  // ---- pipeline: stages st .. st + STAGES - 2 in flight while st is consumed
 #pragma unroll
-  for (int p = 0; p < A_LOADS; ++p) astage[p] = *reinterpret_cast<const uint4*>(a_src[p]);
-#pragma unroll
-  for (int j = 0; j < RN; ++j) {
-    bcur[j] = *reinterpret_cast<const uint4*>(b_src[j]);
-    qcur[j] = q_src[j][0];
-  }
-#pragma unroll
-  for (int p = 0; p < A_LOADS; ++p) *reinterpret_cast<uint4*>(&As[0][a_dst[p]]) = astage[p];
-  __syncthreads();
+  for (int k = 0; k < T::STAGES - 1; ++k) issue(min(st_begin + k, st_end - 1), k);
+  int buf = 0;
+  for (int st = st_begin; st < st_end; ++st) {
+    wait_vmcnt<(T::STAGES - 2) * T::LOADS_PER_STAGE>();  // own loads of stage st done
+    bare_barrier();  // everyone's stage st is in LDS; everyone is done with stage st-1
+    const int nbuf = buf == 0 ? T::STAGES - 1 : buf - 1;  // (st + STAGES - 1) % STAGES
+    const int nst = min(st + T::STAGES - 1, st_end - 1);
+    // this stage's loads of stage nst are spread over the MFMA work below, so
+    // the address unit drains them while the matrix core is busy
+    constexpr int SLOTS = 2 * RN;
 
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    // Prefetch the next group (the last iteration re-reads the last group; its
-    // LDS copy lands in the idle buffer and is never read).
-    const int gn = min(g + 1, G - 1);
-    uint4 bnext[RN];
-    int qnext[RN];
-#pragma unroll
-    for (int p = 0; p < A_LOADS; ++p)
-      astage[p] = *reinterpret_cast<const uint4*>(a_src[p] + static_cast<size_t>(gn) * 128);
+    const int8_t* As = smem + buf * T::STAGE_BYTES;
+    const int8_t* Bs = As + T::A_BYTES;
+    uint2 bw[RN];  // this wave's two words (k-steps 2 wk, 2 wk + 1) per fragment
+    QTables tab[RN];
 #pragma unroll
     for (int j = 0; j < RN; ++j) {
-      bnext[j] = *reinterpret_cast<const uint4*>(b_src[j] + static_cast<size_t>(gn) * 32);
-      qnext[j] = q_src[j][gn];
+      bw[j] = *reinterpret_cast<const uint2*>(Bs + b_slot[j]);
+      tab[j] = make_tables(q_lds[q_pos[j] + st]);
     }
-
-    uint32_t table[RN];  // bytes {-q, 0, +q, 0}
 #pragma unroll
-    for (int j = 0; j < RN; ++j)
-      table[j] = (static_cast<uint32_t>(-qcur[j]) & 0xFFu) | ((static_cast<uint32_t>(qcur[j]) & 0xFFu) << 16);
-
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int ss = 0; ss < 2; ++ss) {
+      const int s = 2 * wk + ss;
       v4i a[RM];
 #pragma unroll
-      for (int i = 0; i < RM; ++i) {
-        const int row = wm * 32 * RM + 32 * i + l32;
-        const int ch = 4 * half + s;
-        a[i] = *reinterpret_cast<const v4i*>(&As[buf][row * 128 + ((ch ^ chunk_swizzle(row)) << 4)]);
-      }
+      for (int i = 0; i < RM; ++i)
+        a[i] = *reinterpret_cast<const v4i*>(As + a_row[i] * kStageK +
+                                             16 * ((4 * half + s) ^ chunk_swizzle(a_row[i])));
 #pragma unroll
       for (int j = 0; j < RN; ++j) {
-        const uint32_t w = (s == 0) ? bcur[j].x : (s == 1) ? bcur[j].y : (s == 2) ? bcur[j].z : bcur[j].w;
-        v4i b;
-        b.x = unpack4(w, 0, table[j]);
-        b.y = unpack4(w, 2, table[j]);
-        b.z = unpack4(w, 4, table[j]);
-        b.w = unpack4(w, 6, table[j]);
+        const v4i b = unpack16(ss == 0 ? bw[j].x : bw[j].y, tab[j]);
 #pragma unroll
         for (int i = 0; i < RM; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b, acc[i][j], 0, 0, 0);
+        // load k of LOADS_PER_STAGE goes after MFMA group k * SLOTS / LOADS
+#pragma unroll
+        for (int k = 0; k < T::LOADS_PER_STAGE; ++k)
+          if ((k * SLOTS) / T::LOADS_PER_STAGE == ss * RN + j) issue_one(k, nst, nbuf);
       }
     }
-
-#pragma unroll
-    for (int p = 0; p < A_LOADS; ++p) *reinterpret_cast<uint4*>(&As[buf ^ 1][a_dst[p]]) = astage[p];
-#pragma unroll
-    for (int j = 0; j < RN; ++j) {
-      bcur[j] = bnext[j];
-      qcur[j] = qnext[j];
-    }
-    __syncthreads();
+    buf = buf == T::STAGES - 1 ? 0 : buf + 1;
   }
+  wait_vmcnt<0>();  // drain the padding loads of the tail before the LDS is reused
 
-  // Epilogue.  32x32 accumulator layout: lane holds column l32; register r
-  // holds row 8 (r / 4) + 4 half + (r % 4).
+  // ---- add the wave pair's partials: wk = 1 hands its accumulators to wk = 0
+  // through the (now idle) pipeline buffers, T::XCH_FRAGS fragments per round.
+  {
+    constexpr int NF = RM * RN;
+    int32_t* xch = reinterpret_cast<int32_t*>(smem);
+    const int pair = wave & 3;
 #pragma unroll
-  for (int j = 0; j < RN; ++j) {
-    const int col = n0 + wn * 32 * RN + 32 * j + l32;
-    if (col >= N) continue;
-    float cscale = 0.0f;
-    if (!OUT_ACC) cscale = smax[col] * (1.0f / 127.0f);
+    for (int f0 = 0; f0 < NF; f0 += T::XCH_FRAGS) {
+      bare_barrier();  // the buffers are free (stage reads / previous round done)
+      if (wk == 1) {
 #pragma unroll
-    for (int i = 0; i < RM; ++i) {
+        for (int f = f0; f < f0 + T::XCH_FRAGS && f < NF; ++f)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 32 * RM + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (row < M) {
-          const size_t o = static_cast<size_t>(row) * N + col;
-          if (OUT_ACC) {
-            static_cast<int32_t*>(out)[o] = acc[i][j][r];
-          } else {
-            static_cast<float*>(out)[o] = static_cast<float>(acc[i][j][r]) * a_scale[row] * cscale;
+          for (int c = 0; c < 4; ++c) {
+            const v16i& a = acc[f / RN][f % RN];
+            const v4i v = {a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]};
+            *reinterpret_cast<v4i*>(xch + ((((f - f0) * 4 + pair) * 4 + c) * 64 + lane) * 4) = v;
           }
-        }
+      }
+      __syncthreads();
+      if (wk == 0) {
+#pragma unroll
+        for (int f = f0; f < f0 + T::XCH_FRAGS && f < NF; ++f)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const v4i v = *reinterpret_cast<const v4i*>(xch + ((((f - f0) * 4 + pair) * 4 + c) * 64 + lane) * 4);
+            v16i& a = acc[f / RN][f % RN];
+            a[4 * c] += v.x;
+            a[4 * c + 1] += v.y;
+            a[4 * c + 2] += v.z;
+            a[4 * c + 3] += v.w;
+          }
       }
     }
   }
+  if (wk != 0) return;
+
+  if (p.splits > 1) {
+    // split-K: store this split's exact partial tile; splitk_reduce_kernel adds
+    // the splits and runs the epilogue.  Slot layout: fragment, 16-byte chunk,
+    // lane (each store instruction writes 1 KB contiguous).
+    int32_t* mine = p.ws_part + (static_cast<size_t>(w.tile) * p.splits + w.split) * T::SLOT_INTS;
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+      for (int j = 0; j < RN; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const v4i v = {acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
+          *reinterpret_cast<v4i*>(mine + ((((wave * RM + i) * RN + j) * 4 + c) * 64 + lane) * 4) = v;
+        }
+    return;
+  }
+  store_tile<RM, FN, OUT_ACC>(acc, p.out, row_scale, col_scale, M, N, m0, n0, wm, wn, lane);
 }
 
-struct TileChoice {
-  int rm, rn;
+// Split-K second pass: one workgroup per block tile, four waves in the same
+// (wm, wn) roles as the GEMM's wk = 0 waves; adds the splits' partial tiles
+// (exact int32) and runs the same epilogue.
+template <int RM, int FN, bool OUT_ACC>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
+  using T = Tile<RM, FN>;
+  constexpr int RN = T::RN;
+  __shared__ float row_scale[T::BM];
+  __shared__ float col_scale[T::BN];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = blockIdx.x;
+  const int m0 = (tile % p.tiles_m) * T::BM, n0 = (tile / p.tiles_m) * T::BN;
+  if (!OUT_ACC) {
+    for (int r = tid; r < T::BM; r += 256) row_scale[r] = p.a_scale[min(m0 + r, p.M - 1)];
+    for (int c = tid; c < T::BN; c += 256) col_scale[c] = p.smax[min(n0 + c, p.N - 1)] * (1.0f / 127.0f);
+  }
+  v16i acc[RM][RN];
+#pragma unroll
+  for (int i = 0; i < RM; ++i)
+#pragma unroll
+    for (int j = 0; j < RN; ++j) acc[i][j] = v16i{0};
+  const int32_t* part = p.ws_part + static_cast<size_t>(tile) * p.splits * T::SLOT_INTS;
+  for (int sp = 0; sp < p.splits; ++sp) {
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+      for (int j = 0; j < RN; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const v4i v = *reinterpret_cast<const v4i*>(
+              part + static_cast<size_t>(sp) * T::SLOT_INTS + ((((wave * RM + i) * RN + j) * 4 + c) * 64 + lane) * 4);
+          acc[i][j][4 * c] += v.x;
+          acc[i][j][4 * c + 1] += v.y;
+          acc[i][j][4 * c + 2] += v.z;
+          acc[i][j][4 * c + 3] += v.w;
+        }
+  }
+  __syncthreads();
+  store_tile<RM, FN, OUT_ACC>(acc, p.out, row_scale, col_scale, p.M, p.N, m0, n0, wave & 1,
+                              wave >> 1, lane);
+}
+
+// ---------------------------------------------------------------- planner
+
+struct Plan {
+  int rm = 0, fn = 0, splits = 1, stages_per_split = 0, tiles_m = 0, tiles_n = 0;
+  size_t slot_ints = 0;
 };
 
-template <int RM, int RN>
-hipError_t launch_tile(const int8_t* x, const float* a_scale, const uint8_t* packed,
-                       const int8_t* q, const float* smax, int M, int N, int K, void* out,
-                       bool out_acc, hipStream_t stream) {
-  const dim3 grid((N + 64 * RN - 1) / (64 * RN), (M + 64 * RM - 1) / (64 * RM));
-  if (out_acc)
-    hipLaunchKernelGGL((gemm_kernel<RM, RN, true>), grid, dim3(256), 0, stream, x, a_scale, packed,
-                       q, smax, M, N, K, out);
-  else
-    hipLaunchKernelGGL((gemm_kernel<RM, RN, false>), grid, dim3(256), 0, stream, x, a_scale,
-                       packed, q, smax, M, N, K, out);
-  return hipGetLastError();
+struct Cfg {
+  int rm, fn;
+};
+constexpr Cfg kCfgs[] = {{1, 4}, {1, 8}, {1, 10}, {2, 4}, {2, 5}, {2, 8},
+                         {2, 9}, {2, 10}, {4, 2}, {4, 4}};
+
+// Estimated cycles of one block tile on one CU.  Per 128-k stage and wave:
+// MFMA issue (32 cycles per 32x32x32, ~10% lost at one wave per SIMD), unpack
+// VALU (11 ops x 4 cycles per column fragment and k-step), LDS traffic
+// (fragment reads of all 4 waves plus the DMA writes, 128 B/clk) and L2->CU
+// traffic (64 B/clk); a stage costs the largest of these plus a fixed
+// barrier/wait overhead.  Then pipeline fill, epilogue stores and, with
+// split-K, the partial-tile traffic.
+double tile_cycles(int rm, int fn, int stages, int splits) {
+  const int rn = (fn + 1) / 2, bm = 64 * rm, bn = 32 * fn;
+  const double mfma = 4.0 * rm * rn * 32.0 * 1.1;
+  const double valu = 4.0 * rn * 9 * 4 + rn * 24.0 + 40.0;
+  const double dma = static_cast<double>(bm) * 128 + bn * 32.0;
+  const double lds = 4.0 * (4.0 * rm * 1024 + rn * 1024.0) / 128.0 + dma / 128.0;
+  const double l2 = dma / 64.0;
+  const double stage = std::max(std::max(mfma, valu), std::max(lds, l2)) + 250.0;
+  double t = stages * stage + 2500.0 + bm * bn * 4.0 / 32.0;
+  if (splits > 1) {
+    // partial tile out, and the reduce kernel's reads of all splits
+    const double slot = 4.0 * 4 * rm * rn * 1024;
+    t += slot / 32.0 + slot / 32.0 + 1500.0;
+  }
+  return t;
 }
 
-// Pick the block tile that minimises the estimated makespan: work per tile
-// over a per-CU rate that grows with the tile (operand reuse), times the
-// number of tiles the busiest CU gets.
-TileChoice choose_tile(int64_t M, int64_t N, const DeviceInfo& dev) {
-  struct Cand {
-    int rm, rn;
-    double rate;
-  };
-  static const Cand cands[] = {{4, 4, 1.00}, {4, 2, 0.85}, {2, 4, 0.85},
-                               {2, 2, 0.70}, {1, 4, 0.55}, {1, 2, 0.45}};
-  const int64_t cus = std::max(1, dev.cu_count);
-  double best = 1e300;
-  TileChoice pick{1, 2};
-  for (const Cand& c : cands) {
-    const int64_t bm = 64 * c.rm, bn = 64 * c.rn;
-    const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-    const int64_t per_cu = (tiles + cus - 1) / cus;
-    const double t = static_cast<double>(per_cu) * static_cast<double>(bm * bn) / c.rate;
-    if (t < best * 0.999) {
-      best = t;
-      pick = {c.rm, c.rn};
+// Choose the block tile and split count that minimise the estimated makespan
+// (tiles are spread evenly, so the busiest CU runs ceil(units / CUs) tiles).
+Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
+  Plan best;
+  double best_t = 1e300;
+  const int n_stages = static_cast<int>(K / kStageK);
+  for (const Cfg& c : kCfgs) {
+    const int bm = 64 * c.rm, bn = 32 * c.fn, rn = (c.fn + 1) / 2;
+    const int64_t tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
+    for (int s = 1; s <= 32; ++s) {
+      const int sps = (n_stages + s - 1) / s;
+      const int splits = (n_stages + sps - 1) / sps;
+      if (splits != s) continue;
+      const int64_t units = tm * tn * splits;
+      if (units > (int64_t{1} << 31) - 1) continue;
+      if (static_cast<int64_t>(bn) * (((sps + 3) & ~3) + 4) > kQTileBytes) continue;
+      const int64_t rounds = (units + cus - 1) / cus;
+      const double t = static_cast<double>(rounds) * tile_cycles(c.rm, c.fn, sps, splits);
+      if (t < best_t * 0.995) {
+        best_t = t;
+        best.rm = c.rm;
+        best.fn = c.fn;
+        best.splits = splits;
+        best.stages_per_split = sps;
+        best.tiles_m = static_cast<int>(tm);
+        best.tiles_n = static_cast<int>(tn);
+        best.slot_ints = static_cast<size_t>(4) * c.rm * rn * 64 * 16;
+      }
     }
   }
-  return pick;
+  return best;
+}
+
+size_t plan_workspace_bytes(const Plan& pl) {
+  if (pl.splits <= 1) return 0;
+  const size_t tiles = static_cast<size_t>(pl.tiles_m) * pl.tiles_n;
+  return tiles * pl.splits * pl.slot_ints * sizeof(int32_t);
+}
+
+template <int RM, int FN>
+hipError_t launch_cfg(const GemmArgs& a, bool out_acc, hipStream_t stream) {
+  const unsigned tiles = static_cast<unsigned>(a.tiles_m) * a.tiles_n;
+  const unsigned grid = tiles * a.splits;
+  if (out_acc)
+    hipLaunchKernelGGL((gemm_kernel<RM, FN, true>), dim3(grid), dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<RM, FN, false>), dim3(grid), dim3(512), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits <= 1) return e;
+  if (out_acc)
+    hipLaunchKernelGGL((splitk_reduce_kernel<RM, FN, true>), dim3(tiles), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((splitk_reduce_kernel<RM, FN, false>), dim3(tiles), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-size_t gemm_workspace_bytes(int64_t, int64_t, int64_t, const DeviceInfo&) { return 0; }
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return plan_workspace_bytes(make_plan(M, N, K, std::max(1, dev.cu_count)));
+}
 
 hipError_t launch_gemm(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
                        const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
-                       void* out, bool out_acc, void*, size_t, const DeviceInfo& dev,
+                       void* out, bool out_acc, void* workspace, size_t, const DeviceInfo& dev,
                        hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  const TileChoice t = choose_tile(M, N, dev);
-  const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-#define TWL_TILE(RM_, RN_)                                                                   \
-  if (t.rm == RM_ && t.rn == RN_)                                                            \
-    return launch_tile<RM_, RN_>(x_i8, a_scale, packed, q, smax, m, n, k, out, out_acc, stream);
-  TWL_TILE(4, 4)
-  TWL_TILE(4, 2)
-  TWL_TILE(2, 4)
-  TWL_TILE(2, 2)
-  TWL_TILE(1, 4)
-  TWL_TILE(1, 2)
-#undef TWL_TILE
+  const Plan pl = make_plan(M, N, K, std::max(1, dev.cu_count));
+  if (pl.rm == 0 || 32 * pl.fn * (((pl.stages_per_split + 3) & ~3) + 4) > kQTileBytes)
+    return hipErrorInvalidConfiguration;  // no plan fits the q block in LDS
+  if (std::getenv("TWL_LOG"))
+    std::fprintf(stderr, "[twl] gemm M=%lld N=%lld K=%lld -> tile %dx%d splits=%d (%d groups each) grid=%d\n",
+                 static_cast<long long>(M), static_cast<long long>(N), static_cast<long long>(K),
+                 64 * pl.rm, 32 * pl.fn, pl.splits, pl.stages_per_split,
+                 pl.tiles_m * pl.tiles_n * pl.splits);
+  GemmArgs a;
+  a.x = x_i8;
+  a.a_scale = a_scale;
+  a.packed = packed;
+  a.q = q;
+  a.smax = smax;
+  a.out = out;
+  a.ws_part = static_cast<int32_t*>(workspace);
+  a.M = static_cast<int>(M);
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  a.tiles_m = pl.tiles_m;
+  a.tiles_n = pl.tiles_n;
+  a.splits = pl.splits;
+  a.stages_per_split = pl.stages_per_split;
+#define TWL_CFG(RM_, FN_) \
+  if (pl.rm == RM_ && pl.fn == FN_) return launch_cfg<RM_, FN_>(a, out_acc, stream);
+  TWL_CFG(1, 4)
+  TWL_CFG(1, 8)
+  TWL_CFG(1, 10)
+  TWL_CFG(2, 4)
+  TWL_CFG(2, 5)
+  TWL_CFG(2, 8)
+  TWL_CFG(2, 9)
+  TWL_CFG(2, 10)
+  TWL_CFG(4, 2)
+  TWL_CFG(4, 4)
+#undef TWL_CFG
   return hipErrorInvalidValue;
 }
 

@@ -17,8 +17,8 @@
 //     addresses -> scalar loads, shared by the 64 rows).
 //   * A wave stages 64 rows x 32 bytes (one 128-group) through LDS with
 //     coalesced 16-byte loads, then each lane reads its own row's 8 words.
-//   * Per word: 3 shifts, 4 ANDs, 4 byte-permutes against {-q, 0, +q}, then
-//     4 v_dot4 per token.  The waves' partial sums are added with LDS integer
+//   * Per word: 1 shift, 4 ANDs, 4 byte-permutes against tables built from
+//     {-q, +q, 0}, then 4 v_dot4 per token.  The waves' partial sums are added with LDS integer
 //     atomics (exact, order independent) before the rescale.
 #include "twl_internal.h"
 
@@ -35,9 +35,32 @@ constexpr int kRowStrideWords = 9;  // 8 words per row + 1 pad: conflict-free co
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(4))) const u32x4 const_u32x4;
 
-__device__ __forceinline__ int unpack4(uint32_t word, int shift, uint32_t table) {
-  const uint32_t sel = (word >> shift) & 0x03030303u;
-  return static_cast<int>(__builtin_amdgcn_perm(0u, table, sel));
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// The 16 int8 weights {code * q} of one packed word (16 codes), as the four
+// dwords of a dot4 operand (dword i = codes 4i .. 4i+3 of the word).  Fields
+// at bits 0-1 / 4-5 of each byte are selectors {0,1,2} into ta = [-q, +q, 0,
+// 0]; fields at bits 2-3 / 6-7, masked in place, are selectors {0,4,8}: byte 0
+// of tb1 (-q), byte 0 of tb0 (+q), or the sign fill of tb1's byte 1, which is
+// 0.  9 VALU operations per 16 codes.
+struct QTables {
+  uint32_t ta, tb0, tb1;
+};
+
+__device__ __forceinline__ QTables make_tables(int qv) {
+  const uint32_t neg = static_cast<uint32_t>(-qv) & 0xFFu;
+  const uint32_t pos = static_cast<uint32_t>(qv) & 0xFFu;
+  return QTables{neg | (pos << 8), pos, neg};
+}
+
+__device__ __forceinline__ v4i unpack16(uint32_t w, const QTables& t) {
+  const uint32_t w4 = w >> 4;
+  v4i b;
+  b.x = static_cast<int>(__builtin_amdgcn_perm(0u, t.ta, w & 0x03030303u));
+  b.y = static_cast<int>(__builtin_amdgcn_perm(t.tb0, t.tb1, w & 0x0C0C0C0Cu));
+  b.z = static_cast<int>(__builtin_amdgcn_perm(0u, t.ta, w4 & 0x03030303u));
+  b.w = static_cast<int>(__builtin_amdgcn_perm(t.tb0, t.tb1, w4 & 0x0C0C0C0Cu));
+  return b;
 }
 
 // MT is the exact number of tokens (1 .. 24).
@@ -100,14 +123,12 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const int8_t* __restrict__ x
     for (int w = 0; w < 8; ++w) words[w] = st[lane * kRowStrideWords + w];
     __builtin_amdgcn_wave_barrier();
 
-    const uint32_t table = (static_cast<uint32_t>(-qv) & 0xFFu) | ((static_cast<uint32_t>(qv) & 0xFFu) << 16);
+    const QTables tab = make_tables(qv);
     const int8_t* xg = x + static_cast<size_t>(g) * 128;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-      const int wq0 = unpack4(words[w], 0, table);
-      const int wq1 = unpack4(words[w], 2, table);
-      const int wq2 = unpack4(words[w], 4, table);
-      const int wq3 = unpack4(words[w], 6, table);
+      const v4i wq = unpack16(words[w], tab);
+      const int wq0 = wq.x, wq1 = wq.y, wq2 = wq.z, wq3 = wq.w;
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         const u32x4 xv = *(const const_u32x4*)(xg + static_cast<size_t>(t) * K + 16 * w);

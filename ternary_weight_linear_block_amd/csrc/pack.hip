@@ -10,10 +10,14 @@
 // division follows and rintf rounds ties to even.
 //
 // 2-bit format (this library's choice; the pages fix only "2 bits per code"):
-// u = code + 1 in {0, 1, 2}; row n is K/16 little-endian 32-bit words and code
-// k = 16w + 4i + b sits in bits [8b + 2i, 8b + 2i + 1] of word w.  With this
-// interleave one shift and one AND turn a word into four bytes holding u for
-// four consecutive k, which the GEMM and GEMV consume directly.
+// field u = 0 for -1, 1 for +1, 2 for 0; row n is K/16 little-endian 32-bit
+// words and code k = 16w + 4i + b sits in bits [8b + 2i, 8b + 2i + 1] of word
+// w.  With this interleave an AND (and one shared shift) turns a word into
+// four bytes holding the fields of four consecutive k, and the field values
+// double as byte-permute selectors: fields at bits 0-1 select bytes {0,1,2}
+// of a {-q, +q, 0} table, fields at bits 2-3 (selectors {0,4,8}) pick -q, +q
+// or the permute's sign-fill byte, which is 0 -- so the GEMM and GEMV expand
+// 16 codes into 16 bytes of code*q with 9 ALU operations.
 //
 // One workgroup per row: the scale reduction, the q row and the packed row are
 // produced together.  The pass is HBM bound (K + K/4 + K/64 bytes per row).
@@ -76,8 +80,10 @@ __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ co
           di &= ~(0xFFu << (8 * b));  // an invalid code packs as 0
         }
       }
-      // per byte: 0xFF -> 0, 0x00 -> 1, 0x01 -> 2, without carries between bytes
-      const uint32_t u = ((di & 0x7F7F7F7Fu) + 0x01010101u) & 0x03030303u;
+      // per byte: code + 1 (0xFF -> 0, 0x00 -> 1, 0x01 -> 2) without carries
+      // between bytes, then swap the two bits: field 0 = -1, 1 = +1, 2 = 0
+      const uint32_t c1 = ((di & 0x7F7F7F7Fu) + 0x01010101u) & 0x03030303u;
+      const uint32_t u = ((c1 & 0x01010101u) << 1) | ((c1 >> 1) & 0x01010101u);
       word |= u << (2 * i);
     }
     pr[w] = word;

@@ -1,0 +1,73 @@
+"""Checks on the generated gfx950 code that need no GPU.
+
+The GEMM issues its direct global->LDS loads from inline asm that sets M0
+itself.  LLVM treats M0 as a reserved register and does not preserve it
+around inline asm, so the kernel is only correct while the compiler never uses
+M0 for anything else.  This test compiles the GEMM to assembly with the
+library's own flags and checks that every M0 write is one of ours (an
+s_mov_b32 from an SGPR followed by a global_load_lds) and that M0 is read by
+nothing else.  It also checks the main loop keeps a single vmcnt wait and no
+accumulator copies.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from ternary_weight_linear_block_amd import build as B
+
+SRC = os.path.join(B.CSRC, "gemm_i8.hip")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "gemm.s"
+    cmd = [B.hipcc()] + [f for f in B.COMMON_FLAGS if f != "-fPIC"] + [
+        "--cuda-device-only", "-S", SRC, "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    return out.read_text()
+
+
+def _kernels(asm_text):
+    """name -> body for each gemm_kernel instantiation."""
+    out = {}
+    for m in re.finditer(r"^(_Z\S*gemm_kernel\S*):[^\n]*\n(.*?)s_endpgm", asm_text, re.S | re.M):
+        out[m.group(1)] = m.group(2)
+    assert len(out) >= 10, f"expected every gemm_kernel instantiation, found {len(out)}"
+    return out
+
+
+def test_m0_only_feeds_our_lds_loads(asm):
+    kernels = _kernels(asm)
+    assert kernels, "no gemm_kernel found in the assembly"
+    for name, body in kernels.items():
+        lines = [ln.strip() for ln in body.splitlines() if ln.strip() and not ln.strip().startswith(";")]
+        for i, ln in enumerate(lines):
+            if "m0" not in ln:
+                continue
+            if ln.startswith("s_mov_b32 m0, s"):
+                nxt = lines[i + 1] if i + 1 < len(lines) else ""
+                assert nxt.startswith("global_load_lds"), (name, ln, nxt)
+            else:
+                pytest.fail(f"{name}: compiler-generated use of m0: {ln}")
+
+
+def test_main_loop_has_one_wait_and_no_accumulator_copies(asm):
+    for name, body in _kernels(asm).items():
+        lines = body.splitlines()
+        loop = None
+        for head in [i for i, ln in enumerate(lines) if "Loop Header" in ln]:
+            end = next(i for i in range(head, len(lines)) if "s_cbranch_scc" in lines[i])
+            cand = "\n".join(lines[head:end + 1])
+            if "v_mfma" in cand:
+                loop = cand
+                break
+        assert loop is not None, name
+        assert loop.count("vmcnt") == 1, name
+        assert "v_accvgpr" not in loop, name
+        assert "v_mfma_i32_32x32x32_i8" in loop, name
