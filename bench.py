@@ -40,6 +40,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 # VALU int8 dot4: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz x 4 MACs x 2 ops
 PEAK_VALU_DOT4_TOPS = 256 * 4 * 16 * 2.4e9 * 8 / 1e12
 CACHE_BUST_BYTES = int(1.1e9)
+COPY_BYTES = 1 << 30
 SECTIONS = ("headline", "down", "decode", "stack")
 
 
@@ -132,7 +133,7 @@ def traffic_for(kernel_src: str, workload: str):
     return None
 
 
-def cpu_baseline(layer, min_s=10.0, max_reps=25):
+def cpu_baseline(layer, min_s=12.0, max_reps=400):
     """The CPU oracle as it stands, on repeated full steps of the workload."""
     import numpy as np
     import oracle.twl_oracle as O
@@ -157,6 +158,19 @@ def cpu_baseline(layer, min_s=10.0, max_reps=25):
             "sample": f"{reps} full steps (rotate_quant_act + ternary_linear, M={layer.M} K={layer.K} "
                       f"N={layer.N}) in {el:.1f} s; numpy, BLAS threads={threads}, "
                       f"affine cores={len(os.sched_getaffinity(0))}"}
+
+
+def copy_calibration(torch) -> int:
+    """y = -x over COPY_BYTES of float32: each launch reads and writes exactly
+    COPY_BYTES, the known size that HBM byte counters are scaled against."""
+    x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": COPY_BYTES,
+                      "copy_calibration_bytes_written": COPY_BYTES, "launches": 3}), flush=True)
+    return 0
 
 
 def section_layer(torch, twl, name, steps, warmup):
@@ -258,6 +272,9 @@ def main(argv=None) -> int:
     ap.add_argument("--sections", default=",".join(SECTIONS),
                     help="comma list of: " + ", ".join(SECTIONS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a copy-like kernel of known traffic (y = -x over 1 GiB of "
+                         "float32, 3 launches) to scale HBM byte counters, then exit")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -272,6 +289,8 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        return copy_calibration(torch)
     sections = [s for s in args.sections.split(",") if s]
     detail = {"device": torch.cuda.get_device_name(0)}
 
