@@ -71,16 +71,50 @@ def n_copies(N: int, K: int) -> int:
     return max(1, -(-CACHE_BUST_BYTES // weight_bytes(N, K)))
 
 
+def graph_time_ms(torch, fn, iters: int, replays: int = 3) -> float:
+    """Mean ms of one fn() call on the GPU: `iters` calls are captured into one
+    HIP graph and the graph is replayed, timed with HIP events on the capture
+    stream.  This removes the host-side launch cost (Python + ctypes, ~10 us
+    per call) that would otherwise hide kernels of a few microseconds."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(iters):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(replays):
+        with torch.cuda.stream(s):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            g.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        best = ms if best is None else min(best, ms)
+    del g
+    return best
+
+
 def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, kernel_iters=50):
     """warmup + timed steps of rotate_quant_act + ternary_linear.
 
-    Returns (ms per step from the wall clock around exactly `steps` steps,
-    mean ms of one rotate_quant_act launch, mean ms of one ternary_linear
-    launch); the per-kernel means come from HIP events around back-to-back
-    launches of that kernel alone on the current stream (weights cycled).
+    Returns (ms per step from the wall clock around exactly `steps` eager
+    steps, mean ms of one rotate_quant_act launch, mean ms of one
+    ternary_linear call); the per-kernel means come from HIP events around a
+    captured graph of `kernel_iters` back-to-back launches of that kernel alone
+    (weights cycled), see graph_time_ms.
     """
     M, K = x.shape
-    N = sets[0][0].shape[0]
+    N = sets[0][2].shape[0]
     x_i8 = torch.empty((M, K), dtype=torch.int8, device="cuda")
     a_scale = torch.empty((M,), dtype=torch.float32, device="cuda")
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
@@ -105,16 +139,15 @@ def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, kernel_iters=50):
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / steps
 
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    ev[0].record()
-    for _ in range(kernel_iters):
-        rotq()
-    ev[1].record()
-    for i in range(kernel_iters):
-        linear(i)
-    ev[2].record()
-    torch.cuda.synchronize()
-    return ms_step, ev[0].elapsed_time(ev[1]) / kernel_iters, ev[1].elapsed_time(ev[2]) / kernel_iters
+    rq = graph_time_ms(torch, rotq, kernel_iters)
+    ctr = [0]
+
+    def linear_next():
+        linear(ctr[0])
+        ctr[0] += 1
+
+    lin = graph_time_ms(torch, linear_next, kernel_iters)
+    return ms_step, rq, lin
 
 
 def traffic_for(kernel_src: str, workload: str):

@@ -84,13 +84,17 @@ twl_status twl_rotate_quant_act(const uint16_t* x, const int8_t* sign, int64_t M
  * pack_ternary -- [P1] Prerequisites and section 4 (load time, once per weight).
  *   smax[n]  = max_g |s[n,g]|                               (fp32, exact)
  *   q[n,g]   = rint((127 * s[n,g]) / smax[n])  in fp32, ties to even; 0 if smax = 0
- *   packed   : 2 bits per code, field u = 0 for -1, 1 for +1, 2 for 0; row n
- *              is K/16 little-endian 32-bit words and code k = 16w + 4i + b
- *              lives in bits [8b + 2i, 8b + 2i + 1] of word w (four codes per
- *              byte).
+ *   packed   : 2 bits per code, field u = 0 for -1, 1 for +1, 2 for 0 (four
+ *              codes per byte).  A row's codes form K/16 little-endian 32-bit
+ *              words, code k = 16w + 4i + b in bits [8b + 2i, 8b + 2i + 1] of
+ *              word w.  The 8 words (32 bytes) of row n and group g = k/128
+ *              are stored at byte ((n/64) * K/128 + g) * 2048 + (n%64) * 32:
+ *              2 KB tiles of 64 rows x one group, ceil(N/64) row blocks, rows
+ *              past N padded with code 0 (bytes 0xAA).  This layout is the
+ *              library's own (the pages fix only 2 bits per code).
  *   code      in : int8 [N, K], values in {-1, 0, +1}
  *   s         in : fp16 bit patterns [N, K/128]
- *   packed    out: uint8 [N, K/4]
+ *   packed    out: uint8, twl_packed_bytes(N, K) bytes
  *   q         out: int8 [N, K/128], |q| <= 127
  *   smax      out: fp32 [N]
  *   bad_codes out: optional (may be NULL) device int32 counter; the number of
@@ -101,9 +105,16 @@ twl_status twl_pack_ternary(const int8_t* code, const uint16_t* s, int64_t N, in
                             hipStream_t stream);
 
 /*
+ * Size in bytes of the packed weight buffer of an N x K layer:
+ * ceil(N/64) * 64 * K/4 (0 for N <= 0 or an invalid K).
+ */
+size_t twl_packed_bytes(int64_t N, int64_t K);
+
+/*
  * Bytes of workspace twl_ternary_linear* may need for this shape on the
  * current device (0 = none; valid for every path).  The workspace holds the
- * GEMM's split-K partial tiles; its contents on entry do not matter (no
+ * GEMM's split-K partial tiles, or the GEMV's per-slice partial sums when it
+ * splits K across workgroups; its contents on entry do not matter (no
  * clearing needed) and calls sharing a workspace must not run concurrently.
  */
 size_t twl_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -115,8 +126,8 @@ size_t twl_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   Prefill sizes run an int8-MFMA GEMM that unpacks the 2-bit codes on chip;
  *   decode batches (M <= TWL_GEMV_MAX_M) run a packed-2-bit GEMV.  Both give
  *   bit-identical acc.
- *   x_i8 [M,K], a_scale [M], packed [N,K/4], q [N,K/128], smax [N] as produced
- *   by the two calls above; y out: fp32 [M, N].
+ *   x_i8 [M,K], a_scale [M], packed (twl_packed_bytes(N,K) bytes), q [N,K/128],
+ *   smax [N] as produced by the two calls above; y out: fp32 [M, N].
  *   workspace: device memory of at least twl_workspace_bytes(M,N,K) bytes; may
  *   be NULL when that is 0.
  */

@@ -35,7 +35,10 @@ Readings taken where the pages are silent (each is listed in the design notes):
   stored exactly as fp32;  R9 an all-zero token gives a_scale = 0, x_i8 = 0, an
   all-zero scale row gives smax = 0, q = 0;  R10 2-bit encoding u = 0 for -1,
   1 for +1, 2 for 0 (3 unused), sixteen codes per little-endian 32-bit word,
-  code k = 16w + 4i + b in bits [8b + 2i, 8b + 2i + 1] of word w;  R11 the
+  code k = 16w + 4i + b in bits [8b + 2i, 8b + 2i + 1] of word w; a row's 32
+  bytes of each 128-group are stored in 2 KB tiles of 64 rows x one group,
+  tile (r, g) at byte (r * K/128 + g) * 2048, row 64r + j at 32 j inside it,
+  rows past N padded with code 0;  R11 the
   epilogue y = acc * a_scale[t] * smax[n] / 127 is evaluated in float64 and
   rounded to fp32 once.
 """
@@ -138,8 +141,19 @@ CODE_TO_FIELD = {-1: 0, 1: 1, 0: 2}
 FIELD_TO_CODE = {v: k for k, v in CODE_TO_FIELD.items()}
 
 
-def pack_codes(code: np.ndarray) -> np.ndarray:
-    """{-1,0,+1} codes [N, K] -> packed bytes [N, K/4] in the R10 layout."""
+ROW_BLOCK = 64                        # rows per weight tile (R10)
+PAD_BYTE = 0xAA                       # four fields of value 2: code 0 (R10)
+
+
+def packed_bytes(N: int, K: int) -> int:
+    """Size of the tiled packed buffer: ceil(N/64) row blocks of 64 rows x K/4 bytes."""
+    return -(-N // ROW_BLOCK) * ROW_BLOCK * K // 4
+
+
+def pack_rows(code: np.ndarray) -> np.ndarray:
+    """{-1,0,+1} codes [N, K] -> one packed row per weight row, [N, K/4] bytes:
+    row n is K/16 little-endian 32-bit words and code k = 16w + 4i + b sits in
+    bits [8b + 2i, 8b + 2i + 1] of word w, field value CODE_TO_FIELD (R10)."""
     code = np.asarray(code)
     N, K = code.shape
     if K % 16:
@@ -158,11 +172,36 @@ def pack_codes(code: np.ndarray) -> np.ndarray:
     return words.astype("<u4").view(np.uint8).reshape(N, K // 4)
 
 
-def unpack_codes(packed: np.ndarray, K: int) -> np.ndarray:
-    """Inverse of pack_codes (test helper): packed [N, K/4] -> int8 codes [N, K]."""
-    packed = np.ascontiguousarray(packed, dtype=np.uint8)
-    N = packed.shape[0]
-    words = packed.view("<u4").reshape(N, K // 16).astype(np.uint64)
+def tile_rows(rows: np.ndarray) -> np.ndarray:
+    """Packed rows [N, K/4] -> the tiled buffer [ceil(N/64), K/128, 64, 32] (R10):
+    tile (r, g) holds the 32 bytes of group g (k = 128g .. 128g + 127) of rows
+    64r .. 64r + 63, one row after another; rows past N are code-0 padding."""
+    rows = np.asarray(rows, dtype=np.uint8)
+    N, KB = rows.shape
+    NB, G = -(-N // ROW_BLOCK), KB // 32
+    full = np.full((NB * ROW_BLOCK, KB), PAD_BYTE, dtype=np.uint8)
+    full[:N] = rows
+    return np.ascontiguousarray(full.reshape(NB, ROW_BLOCK, G, 32).transpose(0, 2, 1, 3))
+
+
+def untile_rows(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Inverse of tile_rows (test helper): tiled buffer (any shape with the
+    right byte count) -> packed rows [N, K/4]."""
+    G = K // GROUP
+    t = np.asarray(packed, dtype=np.uint8).reshape(-1, G, ROW_BLOCK, 32)
+    return np.ascontiguousarray(t.transpose(0, 2, 1, 3).reshape(-1, K // 4)[:N])
+
+
+def pack_codes(code: np.ndarray) -> np.ndarray:
+    """{-1,0,+1} codes [N, K] -> the tiled packed buffer [ceil(N/64), K/128, 64, 32]."""
+    return tile_rows(pack_rows(code))
+
+
+def unpack_rows(rows: np.ndarray, K: int) -> np.ndarray:
+    """Inverse of pack_rows (test helper): packed rows [N, K/4] -> int8 codes [N, K]."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint8)
+    N = rows.shape[0]
+    words = rows.view("<u4").reshape(N, K // 16).astype(np.uint64)
     u = np.zeros((N, K // 16, 4, 4), dtype=np.int64)
     for i in range(4):
         for b in range(4):
@@ -176,8 +215,14 @@ def unpack_codes(packed: np.ndarray, K: int) -> np.ndarray:
     return code
 
 
+def unpack_codes(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Inverse of pack_codes (test helper): tiled buffer -> int8 codes [N, K]."""
+    return unpack_rows(untile_rows(packed, N, K), K)
+
+
 def pack_ternary(code: np.ndarray, s_bits: np.ndarray):
-    """(code [N,K], s fp16 [N,K/128]) -> (packed u8 [N,K/4], q int8 [N,K/128], smax fp32 [N])."""
+    """(code [N,K], s fp16 [N,K/128]) -> (packed tiled u8 [ceil(N/64), K/128, 64, 32],
+    q int8 [N,K/128], smax fp32 [N])."""
     q, smax = decompose_scales(s_bits)
     return pack_codes(code), q, smax
 

@@ -20,7 +20,7 @@ from ._lib import GEMV_MAX_M, GROUP, HBLOCK, MAX_K, PATH_AUTO, PATH_GEMM, PATH_G
 
 __all__ = [
     "rotate_quant_act", "pack_ternary", "ternary_linear", "ternary_linear_acc",
-    "workspace_bytes", "TwlError", "PATH_AUTO", "PATH_GEMM", "PATH_GEMV", "GEMV_MAX_M",
+    "workspace_bytes", "packed_bytes", "TwlError", "PATH_AUTO", "PATH_GEMM", "PATH_GEMV", "GEMV_MAX_M",
     "HBLOCK", "GROUP", "MAX_K", "library",
 ]
 
@@ -72,12 +72,18 @@ def rotate_quant_act(x, sign, out: Optional[Tuple] = None, stream=None):
     return x_i8, a_scale
 
 
+def packed_bytes(N: int, K: int) -> int:
+    """Bytes of the tiled packed weight buffer of an N x K layer."""
+    return int(_lib.load().twl_packed_bytes(N, K))
+
+
 def pack_ternary(code, s, bad_codes=None, stream=None):
-    """code [N, K] int8, s [N, K/128] fp16 -> (packed [N, K/4] uint8, q [N, K/128] int8, smax [N] fp32)."""
+    """code [N, K] int8, s [N, K/128] fp16 -> (packed uint8 [packed_bytes(N, K)] in the
+    tiled layout of include/twl.h, q [N, K/128] int8, smax [N] fp32)."""
     torch = _torch()
     lib = _lib.load()
     N, K = code.shape
-    packed = torch.empty((N, K // 4), dtype=torch.uint8, device=code.device)
+    packed = torch.empty((packed_bytes(N, K),), dtype=torch.uint8, device=code.device)
     q = torch.empty((N, K // GROUP), dtype=torch.int8, device=code.device)
     smax = torch.empty((N,), dtype=torch.float32, device=code.device)
     bad = 0 if bad_codes is None else _dev_ptr(bad_codes, "bad_codes", (torch.int32,))
@@ -98,9 +104,11 @@ def _linear(x_i8, a_scale, packed, q, smax, out_acc: bool, path: int, out=None, 
     torch = _torch()
     lib = _lib.load()
     M, K = x_i8.shape
-    N = packed.shape[0]
-    if packed.shape[1] * 4 != K:
-        raise ValueError(f"packed has {packed.shape[1]} bytes per row, expected K/4 = {K // 4}")
+    N = q.shape[0]
+    if q.dim() != 2 or q.shape[1] * GROUP != K:
+        raise ValueError(f"q has shape {tuple(q.shape)}, expected [N, K/128] with K = {K}")
+    if N > 0 and packed.numel() != packed_bytes(N, K):
+        raise ValueError(f"packed has {packed.numel()} bytes, expected {packed_bytes(N, K)}")
     if out is None:
         out = torch.empty((M, N), dtype=torch.int32 if out_acc else torch.float32, device=x_i8.device)
     need = workspace_bytes(M, N, K)

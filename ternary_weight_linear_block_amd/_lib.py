@@ -25,6 +25,7 @@ _INT = ctypes.c_int
 SIGNATURES = [
     ("twl_rotate_quant_act", _INT, [_P, _P, _I64, _I64, _P, _P, _P]),
     ("twl_pack_ternary", _INT, [_P, _P, _I64, _I64, _P, _P, _P, _P, _P]),
+    ("twl_packed_bytes", _SIZE, [_I64, _I64]),
     ("twl_workspace_bytes", _SIZE, [_I64, _I64, _I64]),
     ("twl_ternary_linear", _INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _SIZE, _P]),
     ("twl_ternary_linear_acc", _INT, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _SIZE, _P]),

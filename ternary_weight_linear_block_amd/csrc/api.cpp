@@ -4,6 +4,7 @@
 #include "twl.h"
 #include "twl_internal.h"
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -100,7 +101,12 @@ extern "C" {
 
 const char* twl_last_error(void) { return g_last_error.c_str(); }
 
-int twl_abi_version(void) { return 1; }
+int twl_abi_version(void) { return 2; }
+
+size_t twl_packed_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || K % TWL_HBLOCK != 0 || K > TWL_MAX_K || N > (int64_t{1} << 30)) return 0;
+  return static_cast<size_t>((N + 63) / 64 * 64) * static_cast<size_t>(K / 4);
+}
 
 twl_status twl_rotate_quant_act(const uint16_t* x, const int8_t* sign, int64_t M, int64_t K,
                                 int8_t* x_i8, float* a_scale, hipStream_t stream) {
@@ -140,8 +146,11 @@ size_t twl_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   twl::DeviceInfo dev;
   if (current_device(&dev) != TWL_OK) return 0;
-  // the GEMM's need, also for M <= TWL_GEMV_MAX_M (TWL_PATH_GEMM may be forced)
-  return twl::gemm_workspace_bytes(M, N, K, dev);
+  // the GEMM's need, also for M <= TWL_GEMV_MAX_M (TWL_PATH_GEMM may be forced),
+  // and the GEMV's where that path may run
+  size_t need = twl::gemm_workspace_bytes(M, N, K, dev);
+  if (M <= TWL_GEMV_MAX_M) need = std::max(need, twl::gemv_workspace_bytes(M, N, K, dev));
+  return need;
 }
 
 twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
@@ -168,17 +177,18 @@ twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const
   twl::DeviceInfo dev;
   TWL_TRY(current_device(&dev));
   const bool use_gemv = path == TWL_PATH_GEMV || (path == TWL_PATH_AUTO && M <= TWL_GEMV_MAX_M);
-  if (use_gemv)
-    return launched(twl::launch_gemv(x_i8, a_scale, packed, q, smax, M, N, K, out, out_acc != 0,
-                                     dev, stream),
-                    "ternary_linear (GEMV)");
-  const size_t need = twl::gemm_workspace_bytes(M, N, K, dev);
+  const size_t need = use_gemv ? twl::gemv_workspace_bytes(M, N, K, dev)
+                               : twl::gemm_workspace_bytes(M, N, K, dev);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need)
       return fail(TWL_EINVAL, "workspace of %zu bytes required (got %zu)", need,
                   workspace == nullptr ? size_t{0} : workspace_bytes);
     if (!aligned16(workspace)) return fail(TWL_EALIGN, "workspace is not 16-byte aligned");
   }
+  if (use_gemv)
+    return launched(twl::launch_gemv(x_i8, a_scale, packed, q, smax, M, N, K, out, out_acc != 0,
+                                     workspace, workspace_bytes, dev, stream),
+                    "ternary_linear (GEMV)");
   return launched(twl::launch_gemm(x_i8, a_scale, packed, q, smax, M, N, K, out, out_acc != 0,
                                    workspace, workspace_bytes, dev, stream),
                   "ternary_linear (GEMM)");

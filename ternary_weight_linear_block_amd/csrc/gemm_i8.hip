@@ -35,7 +35,8 @@
 //     holds BM x 128 bytes of x_i8 (8 lanes per row; 16-byte chunks
 //     XOR-swizzled by row so the column-wise ds_read_b128 hits distinct banks)
 //     and BN x 32 bytes of packed weights (2 lanes per weight row, the two
-//     16-byte halves parity-swizzled by column).  Each load instruction thus
+//     16-byte halves parity-swizzled by column; in the tiled weight layout
+//     these are whole 2 KB tiles of 64 rows, contiguous in memory).  Each load instruction thus
 //     touches few cache lines; the q block of the tile is copied to LDS once
 //     up front.  Every wave issues the same static set of loads per stage,
 //     waits only for its own (vmcnt), and a bare s_barrier publishes the
@@ -94,6 +95,16 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
 __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
                :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory", "m0");
+}
+
+// A wave-uniform pointer forced into SGPRs (the inline-asm loads take their
+// base address as an SGPR pair; 64-bit address arithmetic may otherwise be
+// left in VGPRs).
+__device__ __forceinline__ const void* sgpr_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 // LDS byte offset of a __shared__ object (generic -> local address space).
@@ -251,7 +262,6 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs p) {
   const WorkItem w = work_item(blockIdx.x, p.tiles_m, p.tiles_n, p.splits, T::BM, BN);
   const int m0 = w.m0, n0 = w.n0;
   const int M = p.M, N = p.N, K = p.K;
-  const size_t KB = static_cast<size_t>(K) >> 2;
   const int G = K >> 7;
   const int st_begin = w.split * p.stages_per_split;
   const int st_end = min(G, st_begin + p.stages_per_split);
@@ -284,7 +294,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs p) {
   // repeats an earlier one: same data to the same LDS bytes), which keeps the
   // per-stage load count static for the vmcnt bookkeeping.
   const int8_t* x_tile = p.x + static_cast<size_t>(m0) * K;
-  const uint8_t* w_tile = p.packed + static_cast<size_t>(n0) * KB;
+  // weights: tiled layout, tile (row block r, group g) of 64 rows x 32 bytes at
+  // byte (r * G + g) * 2048; the tile base is this workgroup's first row block
+  const uint8_t* w_tile = p.packed + static_cast<size_t>(n0 >> 6) * G * 2048;
   // A: instruction ia covers rows 8 ia .. 8 ia + 7 (1 KB, 8 lanes per 128-byte
   // row); lane -> row, 16-B slot, holding chunk slot ^ swizzle(row)
   uint32_t a_off[T::A_PER_WAVE];
@@ -307,7 +319,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs p) {
     const int ib = (wave + 8 * i) % T::B_INSTR;
     const int col = 32 * ib + (lane >> 1);
     const int h = (lane & 1) ^ ((col >> 3) & 1);
-    b_off[i] = static_cast<uint32_t>((min(n0 + col, N - 1) - n0) * KB + 16 * h);
+    const int nc = min(n0 + col, N - 1);
+    b_off[i] = static_cast<uint32_t>(((nc >> 6) - (n0 >> 6)) * G * 2048 + (nc & 63) * 32 + 16 * h);
     b_lds[i] = T::A_BYTES + ib * 1024;
   }
 
@@ -318,7 +331,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs p) {
     if (i < T::A_PER_WAVE)
       dma16(x_tile + static_cast<size_t>(st) * kStageK, a_off[i], base + a_lds[i]);
     else
-      dma16(w_tile + static_cast<size_t>(st) * (kStageK / 4), b_off[i - T::A_PER_WAVE],
+      dma16(sgpr_ptr(w_tile + static_cast<size_t>(st) * 2048), b_off[i - T::A_PER_WAVE],
             base + b_lds[i - T::A_PER_WAVE]);
   };
   auto issue = [&](int st, int buf) {

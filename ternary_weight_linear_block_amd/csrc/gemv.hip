@@ -11,23 +11,34 @@
 // bit-exact with the GEMM because both compute the same integer sum.
 //
 // gfx950 mapping
-//   * One workgroup owns 64 weight rows (lane l <-> row n0 + l) and splits the
-//     K groups across its waves, so each lane keeps only M int32 accumulators
-//     and the activations of a step are the same for the whole wave (uniform
-//     addresses -> scalar loads, shared by the 64 rows).
-//   * A wave stages 64 rows x 32 bytes (one 128-group) through LDS with
-//     coalesced 16-byte loads, then each lane reads its own row's 8 words.
-//   * Per word: 1 shift, 4 ANDs, 4 byte-permutes against tables built from
-//     {-q, +q, 0}, then 4 v_dot4 per token.  The waves' partial sums are added with LDS integer
-//     atomics (exact, order independent) before the rescale.
+//   * A wave owns 64 weight rows (lane l <-> row n0 + l) and one chunk of GPW
+//     consecutive 128-groups of K.  It issues the loads of its whole chunk up
+//     front (GPW x 2 KB per wave in flight), so the memory system sees the
+//     matrix as one burst instead of a latency-bound sequence of small reads.
+//   * In the tiled weight layout a wave's group is one contiguous 2 KB tile,
+//     read with two 1 KB loads; one half-wave swap (v_permlane32_swap, 4 VALU
+//     operations per group) leaves each lane with its own row's 8 words; no
+//     LDS round trip in the loop.
+//   * The activations of a group are the same for all 64 rows: they are read
+//     at wave-uniform addresses through the constant address space (scalar
+//     loads, one copy in SGPRs per wave).
+//   * Per packed word: 1 shift, 4 ANDs, 4 byte-permutes against tables built
+//     from {-q, +q, 0}, then 4 v_dot4 per token.
+//   * A workgroup holds the waves of consecutive chunks of one 64-row block and
+//     adds their partial sums with LDS integer atomics (exact).  When there are
+//     too few row blocks to give every CU a workgroup, K is also split across
+//     workgroups ("slices"): each slice writes int32 partial sums to the
+//     workspace and a second kernel adds them in a fixed order and rescales.
 #include "twl_internal.h"
 
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 
 namespace twl {
 namespace {
 
-constexpr int kRowStrideWords = 9;  // 8 words per row + 1 pad: conflict-free column reads
+constexpr int kMaxWaves = 8;
 
 // Activations are read at wave-uniform addresses; reading them through the
 // constant address space makes them scalar loads (one copy in SGPRs for the
@@ -63,153 +74,283 @@ __device__ __forceinline__ v4i unpack16(uint32_t w, const QTables& t) {
   return b;
 }
 
-// MT is the exact number of tokens (1 .. 24).
-template <int MT, bool OUT_ACC>
-__global__ __launch_bounds__(1024) void gemv_kernel(const int8_t* __restrict__ x,
-                                                    const float* __restrict__ a_scale,
-                                                    const uint8_t* __restrict__ packed,
-                                                    const int8_t* __restrict__ q,
-                                                    const float* __restrict__ smax, int N, int K,
-                                                    void* __restrict__ out) {
+struct GemvArgs {
+  const int8_t* x;
+  const float* a_scale;
+  const uint8_t* packed;
+  const int8_t* q;
+  const float* smax;
+  void* out;          // float y [M,N] or int32 acc [M,N]
+  int32_t* part;      // [slices][M][N] int32 partial sums when slices > 1
+  int N, K, G;        // G = K / 128
+  int n_rb;           // 64-row blocks
+  int nch;            // chunks of GPW groups along K
+  int slices;         // workgroups per row block (K split across workgroups)
+  int out_acc;
+};
+
+// v_permlane32_swap_b32 exchanges lanes 32..63 of its first operand with lanes
+// 0..31 of its second: applied to each dword of two 16-byte values it moves
+// lo's upper-lane half into hi's lower lanes and back.
+__device__ __forceinline__ void swap_halves(uint4& lo, uint4& hi) {
+  auto r0 = __builtin_amdgcn_permlane32_swap(lo.x, hi.x, false, false);
+  auto r1 = __builtin_amdgcn_permlane32_swap(lo.y, hi.y, false, false);
+  auto r2 = __builtin_amdgcn_permlane32_swap(lo.z, hi.z, false, false);
+  auto r3 = __builtin_amdgcn_permlane32_swap(lo.w, hi.w, false, false);
+  lo = make_uint4(r0[0], r1[0], r2[0], r3[0]);
+  hi = make_uint4(r0[1], r1[1], r2[1], r3[1]);
+}
+
+// MT is the exact number of tokens (1 .. 24); GPW the groups per wave chunk
+// (G is a multiple of 8, so every chunk is whole).  Static LDS: MT x 64 ints
+// for the cross-wave sums.
+template <int MT, int GPW>
+__global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
+  __shared__ int red[MT * 64];
   const int lane = threadIdx.x & 63;
   // wave index as a scalar: everything derived from it (the K range, the
   // activation addresses) is then known to be wave-uniform
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
-  const int n0 = blockIdx.x * 64;
-  const int G = K >> 7;
-  const size_t KB = static_cast<size_t>(K) >> 2;
+  const int rb = blockIdx.x % a.n_rb;
+  const int slice = blockIdx.x / a.n_rb;
+  const int n0 = rb * 64;
+  const int N = a.N, K = a.K, G = a.G;
 
-  __shared__ uint32_t stage[16][64 * kRowStrideWords];
-  __shared__ int red[MT][64];
-  for (int i = threadIdx.x; i < MT * 64; i += blockDim.x) (&red[0][0])[i] = 0;
+  for (int i = threadIdx.x; i < MT * 64; i += blockDim.x) red[i] = 0;
   __syncthreads();
 
-  // contiguous range of 128-groups for this wave
-  const int g_begin = (G * wave) / nw;
-  const int g_end = (G * (wave + 1)) / nw;
+  const int c_lo = (slice * a.nch) / a.slices;
+  const int c_hi = ((slice + 1) * a.nch) / a.slices;
+  const int chunk = c_lo + wave;
 
-  // coalesced staging: 16-byte piece p (0..127) of the wave's 64x32-byte tile
-  // is row p / 2, half p % 2; each lane moves pieces lane and lane + 64.
-  const int r0 = lane >> 1, r1 = (lane + 64) >> 1;
-  const int hp = lane & 1;
-  const uint8_t* src0 = packed + static_cast<size_t>(min(n0 + r0, N - 1)) * KB + hp * 16;
-  const uint8_t* src1 = packed + static_cast<size_t>(min(n0 + r1, N - 1)) * KB + hp * 16;
-  uint32_t* st = stage[wave];
-  const int my_row = min(n0 + lane, N - 1);
-  const int8_t* qrow = q + static_cast<size_t>(my_row) * G;
+  if (chunk < c_hi) {
+    const int g0 = chunk * GPW;
+    // The group's weights are one contiguous 2 KB tile (64 rows x 32 bytes;
+    // rows past N are code-0 padding), read with two 1 KB loads: in load A
+    // lane l < 32 takes bytes 0-15 of row l and lane l >= 32 bytes 16-31 of
+    // row l - 32; load B the same for rows 32..63.  One half-swap (lanes
+    // 32..63 of A with lanes 0..31 of B) then leaves lane l with bytes 0-15
+    // (A) and 16-31 (B) of its own row n0 + l.
+    const int hsel = lane >> 5;
+    const int rlo = lane & 31;
+    const uint8_t* srcA = a.packed + static_cast<size_t>(rb) * G * 2048 + rlo * 32 + hsel * 16;
+    const uint8_t* srcB = srcA + 1024;
+    const int8_t* qrow = a.q + static_cast<size_t>(min(n0 + lane, N - 1)) * G + g0;
 
-  int acc[MT];
+    // the whole chunk in flight at once
+    uint4 dA[GPW], dB[GPW];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = 0;
+    for (int j = 0; j < GPW; ++j) {
+      const size_t g = static_cast<size_t>(g0 + j);
+      dA[j] = *reinterpret_cast<const uint4*>(srcA + g * 2048);
+      dB[j] = *reinterpret_cast<const uint4*>(srcB + g * 2048);
+    }
+    int8_t qv[GPW];
+    if (GPW == 8) {
+      const uint2 qq = *reinterpret_cast<const uint2*>(qrow);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qv[j] = static_cast<int8_t>(qq.x >> (8 * j));
+#pragma unroll
+      for (int j = 4; j < GPW; ++j) qv[j] = static_cast<int8_t>(qq.y >> (8 * (j - 4)));
+    } else {
+      const uint32_t qq = *reinterpret_cast<const uint32_t*>(qrow);
+#pragma unroll
+      for (int j = 0; j < GPW; ++j) qv[j] = static_cast<int8_t>(qq >> (8 * j));
+    }
 
-  for (int g = g_begin; g < g_end; ++g) {
-    const uint4 p0 = *reinterpret_cast<const uint4*>(src0 + static_cast<size_t>(g) * 32);
-    const uint4 p1 = *reinterpret_cast<const uint4*>(src1 + static_cast<size_t>(g) * 32);
-    const int qv = qrow[g];
-    st[r0 * kRowStrideWords + hp * 4 + 0] = p0.x;
-    st[r0 * kRowStrideWords + hp * 4 + 1] = p0.y;
-    st[r0 * kRowStrideWords + hp * 4 + 2] = p0.z;
-    st[r0 * kRowStrideWords + hp * 4 + 3] = p0.w;
-    st[r1 * kRowStrideWords + hp * 4 + 0] = p1.x;
-    st[r1 * kRowStrideWords + hp * 4 + 1] = p1.y;
-    st[r1 * kRowStrideWords + hp * 4 + 2] = p1.z;
-    st[r1 * kRowStrideWords + hp * 4 + 3] = p1.w;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    uint32_t words[8];
+    // small M: two accumulator chains per token so consecutive dot4s do not
+    // wait on each other
+    constexpr int NA = MT <= 4 ? 2 : 1;
+    int acc[NA][MT];
 #pragma unroll
-    for (int w = 0; w < 8; ++w) words[w] = st[lane * kRowStrideWords + w];
-    __builtin_amdgcn_wave_barrier();
+    for (int c = 0; c < NA; ++c)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[c][t] = 0;
 
-    const QTables tab = make_tables(qv);
-    const int8_t* xg = x + static_cast<size_t>(g) * 128;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const v4i wq = unpack16(words[w], tab);
-      const int wq0 = wq.x, wq1 = wq.y, wq2 = wq.z, wq3 = wq.w;
+    for (int j = 0; j < GPW; ++j) {
+      uint4 lo = dA[j], hi = dB[j];
+      swap_halves(lo, hi);
+      const uint32_t words[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      const QTables tab = make_tables(qv[j]);
+      const int8_t* xg = a.x + static_cast<size_t>(g0 + j) * 128;
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const u32x4 xv = *(const const_u32x4*)(xg + static_cast<size_t>(t) * K + 16 * w);
-        int a = acc[t];
-        a = __builtin_amdgcn_sdot4(wq0, static_cast<int>(xv.x), a, false);
-        a = __builtin_amdgcn_sdot4(wq1, static_cast<int>(xv.y), a, false);
-        a = __builtin_amdgcn_sdot4(wq2, static_cast<int>(xv.z), a, false);
-        a = __builtin_amdgcn_sdot4(wq3, static_cast<int>(xv.w), a, false);
-        acc[t] = a;
+      for (int w = 0; w < 8; ++w) {
+        const v4i wq = unpack16(words[w], tab);
+        const int wq0 = wq.x, wq1 = wq.y, wq2 = wq.z, wq3 = wq.w;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const u32x4 xv = *(const const_u32x4*)(xg + static_cast<size_t>(t) * K + 16 * w);
+          int s = acc[w % NA][t];
+          s = __builtin_amdgcn_sdot4(wq0, static_cast<int>(xv.x), s, false);
+          s = __builtin_amdgcn_sdot4(wq1, static_cast<int>(xv.y), s, false);
+          s = __builtin_amdgcn_sdot4(wq2, static_cast<int>(xv.z), s, false);
+          s = __builtin_amdgcn_sdot4(wq3, static_cast<int>(xv.w), s, false);
+          acc[w % NA][t] = s;
+        }
       }
     }
-  }
-
-  // exact cross-wave reduction (integer LDS atomics), then the rescale
+    // exact cross-wave reduction (integer LDS atomics, order independent)
 #pragma unroll
-  for (int t = 0; t < MT; ++t) atomicAdd(&red[t][lane], acc[t]);
+    for (int t = 0; t < MT; ++t) {
+      int s = acc[0][t];
+#pragma unroll
+      for (int c = 1; c < NA; ++c) s += acc[c][t];
+      atomicAdd(&red[t * 64 + lane], s);
+    }
+  }
   __syncthreads();
+
   const int n = n0 + lane;
+  if (n >= N) return;
   for (int t = wave; t < MT; t += nw) {
-    const int s = red[t][lane];
-    if (n < N) {
+    const int s = red[t * 64 + lane];
+    if (a.slices > 1) {
+      a.part[(static_cast<size_t>(slice) * MT + t) * N + n] = s;
+    } else {
       const size_t o = static_cast<size_t>(t) * N + n;
-      if (OUT_ACC)
-        static_cast<int32_t*>(out)[o] = s;
+      if (a.out_acc)
+        static_cast<int32_t*>(a.out)[o] = s;
       else
-        static_cast<float*>(out)[o] = static_cast<float>(s) * a_scale[t] * (smax[n] * (1.0f / 127.0f));
+        static_cast<float*>(a.out)[o] =
+            static_cast<float>(s) * a.a_scale[t] * (a.smax[n] * (1.0f / 127.0f));
     }
   }
 }
 
+// Sum of the slices' partial sums in slice order, then the rescale.
+__global__ __launch_bounds__(256) void gemv_reduce_kernel(const int32_t* __restrict__ part,
+                                                          int slices, int M, int N,
+                                                          const float* __restrict__ a_scale,
+                                                          const float* __restrict__ smax,
+                                                          void* __restrict__ out, int out_acc) {
+  const size_t total = static_cast<size_t>(M) * N;
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += stride) {
+    int s = 0;
+    for (int sl = 0; sl < slices; ++sl) s += part[static_cast<size_t>(sl) * total + i];
+    if (out_acc) {
+      static_cast<int32_t*>(out)[i] = s;
+    } else {
+      const int t = static_cast<int>(i / static_cast<size_t>(N));
+      const int n = static_cast<int>(i - static_cast<size_t>(t) * N);
+      static_cast<float*>(out)[i] = static_cast<float>(s) * a_scale[t] * (smax[n] * (1.0f / 127.0f));
+    }
+  }
+}
+
+struct GemvPlan {
+  int gpw = 8;     // groups per wave chunk (8 or 4)
+  int nw = 1;      // waves per workgroup
+  int slices = 1;  // workgroups per 64-row block
+  int nch = 1;     // chunks along K
+  int n_rb = 1;
+};
+
+GemvPlan make_plan(int64_t N, int64_t K, const DeviceInfo& dev) {
+  const int G = static_cast<int>(K >> 7);
+  const int n_rb = static_cast<int>((N + 63) / 64);
+  const int cus = std::max(1, dev.cu_count);
+  GemvPlan best;
+  for (int gpw : {8, 4}) {
+    GemvPlan p;
+    p.gpw = gpw;
+    p.n_rb = n_rb;
+    p.nch = G / gpw;   // G is a multiple of 8
+    // enough workgroups that every CU gets one, at most kMaxWaves waves each
+    p.slices = std::min(p.nch, std::max(1, (cus + n_rb - 1) / n_rb));
+    while ((p.nch + p.slices - 1) / p.slices > kMaxWaves) ++p.slices;
+    p.nw = (p.nch + p.slices - 1) / p.slices;
+    best = p;
+    // prefer the deeper chunk while it still leaves >= 4 waves per CU
+    if (static_cast<int64_t>(n_rb) * p.slices * p.nw >= 4 * static_cast<int64_t>(cus)) break;
+  }
+  return best;
+}
+
 template <int MT>
-hipError_t launch_mt(const int8_t* x, const float* a_scale, const uint8_t* packed, const int8_t* q,
-                     const float* smax, int N, int K, void* out, bool out_acc,
-                     hipStream_t stream) {
-  const int G = K >> 7;
-  const int nw = std::max(1, std::min(16, G / 4));
-  const dim3 grid((N + 63) / 64);
-  if (out_acc)
-    hipLaunchKernelGGL((gemv_kernel<MT, true>), grid, dim3(64 * nw), 0, stream, x, a_scale, packed,
-                       q, smax, N, K, out);
+hipError_t launch_mt(GemvArgs a, const GemvPlan& pl, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(pl.n_rb * pl.slices));
+  const dim3 block(64 * pl.nw);
+  if (pl.gpw == 8)
+    hipLaunchKernelGGL((gemv_kernel<MT, 8>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((gemv_kernel<MT, false>), grid, dim3(64 * nw), 0, stream, x, a_scale,
-                       packed, q, smax, N, K, out);
+    hipLaunchKernelGGL((gemv_kernel<MT, 4>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  const GemvPlan pl = make_plan(N, K, dev);
+  if (pl.slices <= 1) return 0;
+  return static_cast<size_t>(pl.slices) * static_cast<size_t>(M) * static_cast<size_t>(N) * 4;
+}
+
 hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
                        const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
-                       void* out, bool out_acc, const DeviceInfo&, hipStream_t stream) {
+                       void* out, bool out_acc, void* workspace, size_t workspace_bytes,
+                       const DeviceInfo& dev, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  const int n = static_cast<int>(N), k = static_cast<int>(K);
+  const GemvPlan pl = make_plan(N, K, dev);
+  if (pl.slices > 1 && workspace_bytes < gemv_workspace_bytes(M, N, K, dev))
+    return hipErrorInvalidValue;
+  if (std::getenv("TWL_LOG"))
+    std::fprintf(stderr, "[twl] gemv M=%lld N=%lld K=%lld -> %d groups/wave, %d waves/WG, %d slices, grid=%d\n",
+                 static_cast<long long>(M), static_cast<long long>(N), static_cast<long long>(K),
+                 pl.gpw, pl.nw, pl.slices, pl.n_rb * pl.slices);
+  GemvArgs a;
+  a.x = x_i8;
+  a.a_scale = a_scale;
+  a.packed = packed;
+  a.q = q;
+  a.smax = smax;
+  a.out = out;
+  a.part = static_cast<int32_t*>(workspace);
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  a.G = static_cast<int>(K >> 7);
+  a.n_rb = pl.n_rb;
+  a.nch = pl.nch;
+  a.slices = pl.slices;
+  a.out_acc = out_acc ? 1 : 0;
+  hipError_t e = hipErrorInvalidValue;
   switch (static_cast<int>(M)) {
-    case 1: return launch_mt<1>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 2: return launch_mt<2>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 3: return launch_mt<3>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 4: return launch_mt<4>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 5: return launch_mt<5>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 6: return launch_mt<6>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 7: return launch_mt<7>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 8: return launch_mt<8>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 9: return launch_mt<9>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 10: return launch_mt<10>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 11: return launch_mt<11>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 12: return launch_mt<12>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 13: return launch_mt<13>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 14: return launch_mt<14>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 15: return launch_mt<15>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 16: return launch_mt<16>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 17: return launch_mt<17>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 18: return launch_mt<18>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 19: return launch_mt<19>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 20: return launch_mt<20>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 21: return launch_mt<21>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 22: return launch_mt<22>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 23: return launch_mt<23>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    case 24: return launch_mt<24>(x_i8, a_scale, packed, q, smax, n, k, out, out_acc, stream);
-    default: break;
+    case 1: e = launch_mt<1>(a, pl, stream); break;
+    case 2: e = launch_mt<2>(a, pl, stream); break;
+    case 3: e = launch_mt<3>(a, pl, stream); break;
+    case 4: e = launch_mt<4>(a, pl, stream); break;
+    case 5: e = launch_mt<5>(a, pl, stream); break;
+    case 6: e = launch_mt<6>(a, pl, stream); break;
+    case 7: e = launch_mt<7>(a, pl, stream); break;
+    case 8: e = launch_mt<8>(a, pl, stream); break;
+    case 9: e = launch_mt<9>(a, pl, stream); break;
+    case 10: e = launch_mt<10>(a, pl, stream); break;
+    case 11: e = launch_mt<11>(a, pl, stream); break;
+    case 12: e = launch_mt<12>(a, pl, stream); break;
+    case 13: e = launch_mt<13>(a, pl, stream); break;
+    case 14: e = launch_mt<14>(a, pl, stream); break;
+    case 15: e = launch_mt<15>(a, pl, stream); break;
+    case 16: e = launch_mt<16>(a, pl, stream); break;
+    case 17: e = launch_mt<17>(a, pl, stream); break;
+    case 18: e = launch_mt<18>(a, pl, stream); break;
+    case 19: e = launch_mt<19>(a, pl, stream); break;
+    case 20: e = launch_mt<20>(a, pl, stream); break;
+    case 21: e = launch_mt<21>(a, pl, stream); break;
+    case 22: e = launch_mt<22>(a, pl, stream); break;
+    case 23: e = launch_mt<23>(a, pl, stream); break;
+    case 24: e = launch_mt<24>(a, pl, stream); break;
+    default: return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
+  if (e != hipSuccess || pl.slices <= 1) return e;
+  const size_t total = static_cast<size_t>(M) * static_cast<size_t>(N);
+  const unsigned blocks = static_cast<unsigned>(std::min<size_t>((total + 255) / 256, 4096));
+  hipLaunchKernelGGL(gemv_reduce_kernel, dim3(blocks), dim3(256), 0, stream, a.part, pl.slices,
+                     static_cast<int>(M), a.N, a_scale, smax, out, a.out_acc);
+  return hipGetLastError();
 }
 
 }  // namespace twl

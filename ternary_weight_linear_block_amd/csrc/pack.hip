@@ -10,17 +10,25 @@
 // division follows and rintf rounds ties to even.
 //
 // 2-bit format (this library's choice; the pages fix only "2 bits per code"):
-// field u = 0 for -1, 1 for +1, 2 for 0; row n is K/16 little-endian 32-bit
-// words and code k = 16w + 4i + b sits in bits [8b + 2i, 8b + 2i + 1] of word
-// w.  With this interleave an AND (and one shared shift) turns a word into
-// four bytes holding the fields of four consecutive k, and the field values
-// double as byte-permute selectors: fields at bits 0-1 select bytes {0,1,2}
-// of a {-q, +q, 0} table, fields at bits 2-3 (selectors {0,4,8}) pick -q, +q
-// or the permute's sign-fill byte, which is 0 -- so the GEMM and GEMV expand
-// 16 codes into 16 bytes of code*q with 9 ALU operations.
+// field u = 0 for -1, 1 for +1, 2 for 0; within a row, code k = 16w + 4i + b
+// sits in bits [8b + 2i, 8b + 2i + 1] of little-endian 32-bit word w.  With
+// this interleave an AND (and one shared shift) turns a word into four bytes
+// holding the fields of four consecutive k, and the field values double as
+// byte-permute selectors: fields at bits 0-1 select bytes {0,1,2} of a
+// {-q, +q, 0} table, fields at bits 2-3 (selectors {0,4,8}) pick -q, +q or the
+// permute's sign-fill byte, which is 0 -- so the GEMM and GEMV expand 16 codes
+// into 16 bytes of code*q with 9 ALU operations.
 //
-// One workgroup per row: the scale reduction, the q row and the packed row are
-// produced together.  The pass is HBM bound (K + K/4 + K/64 bytes per row).
+// Tiled layout: the 32 bytes (8 words) of each row and 128-group are stored in
+// 2048-byte tiles of 64 rows x one group; tile (r, g) starts at byte
+// (r * K/128 + g) * 2048 and holds rows 64r .. 64r + 63 in order.  A decode
+// wave that owns 64 rows then reads one contiguous 2 KB tile per group, and a
+// GEMM stage's weight slice is a few contiguous tiles.  The buffer has
+// ceil(N/64) row blocks; rows past N are padding with code 0 (byte 0xAA).
+//
+// One workgroup per row (padding rows included): the scale reduction, the q
+// row and the packed row are produced together.  The pass is HBM bound
+// (K + K/4 + K/64 bytes per row).
 #include "twl_internal.h"
 
 namespace twl {
@@ -31,16 +39,24 @@ __device__ __forceinline__ float fp16_bits_to_float(uint16_t bits) {
 }
 
 __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ code,
-                                                   const uint16_t* __restrict__ s, int K,
+                                                   const uint16_t* __restrict__ s, int N, int K,
                                                    uint8_t* __restrict__ packed,
                                                    int8_t* __restrict__ q,
                                                    float* __restrict__ smax,
                                                    int32_t* __restrict__ bad_codes) {
-  const int n = blockIdx.x;
+  const int n = blockIdx.x;  // 0 .. ceil(N/64) * 64 - 1
   const int tid = threadIdx.x;
   const int G = K >> 7;
-  const uint16_t* sr = s + static_cast<size_t>(n) * G;
+  uint8_t* tile_row = packed + static_cast<size_t>(n >> 6) * G * 2048 + (n & 63) * 32;
 
+  if (n >= N) {  // padding row of the last row block: code 0 everywhere
+    for (int w = tid; w < (K >> 4); w += 256)
+      *reinterpret_cast<uint32_t*>(tile_row + static_cast<size_t>(w >> 3) * 2048 + (w & 7) * 4) =
+          0xAAAAAAAAu;
+    return;
+  }
+
+  const uint16_t* sr = s + static_cast<size_t>(n) * G;
   // smax[n] = max_g |s[n,g]|
   float m = 0.0f;
   for (int g = tid; g < G; g += 256) m = fmaxf(m, fabsf(fp16_bits_to_float(sr[g])));
@@ -61,9 +77,9 @@ __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ co
     qr[g] = static_cast<int8_t>(static_cast<int>(r));
   }
 
-  // 2-bit packing, one 16-code word per thread iteration
+  // 2-bit packing, one 16-code word per thread iteration; word w of the row is
+  // word w % 8 of its row slot in tile (n / 64, w / 8)
   const int8_t* cr = code + static_cast<size_t>(n) * K;
-  uint32_t* pr = reinterpret_cast<uint32_t*>(packed + static_cast<size_t>(n) * (K >> 2));
   int nbad = 0;
   for (int w = tid; w < (K >> 4); w += 256) {
     const uint4 c = *reinterpret_cast<const uint4*>(cr + 16 * w);
@@ -86,7 +102,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ co
       const uint32_t u = ((c1 & 0x01010101u) << 1) | ((c1 >> 1) & 0x01010101u);
       word |= u << (2 * i);
     }
-    pr[w] = word;
+    *reinterpret_cast<uint32_t*>(tile_row + static_cast<size_t>(w >> 3) * 2048 + (w & 7) * 4) = word;
   }
 
   if (bad_codes != nullptr) {
@@ -107,8 +123,9 @@ hipError_t launch_pack(const int8_t* code, const uint16_t* s, int64_t N, int64_t
                        uint8_t* packed, int8_t* q, float* smax, int32_t* bad_codes,
                        hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>(N)), dim3(256), 0, stream, code, s,
-                     static_cast<int>(K), packed, q, smax, bad_codes);
+  const int64_t rows = (N + 63) / 64 * 64;
+  hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>(rows)), dim3(256), 0, stream, code, s,
+                     static_cast<int>(N), static_cast<int>(K), packed, q, smax, bad_codes);
   return hipGetLastError();
 }
 

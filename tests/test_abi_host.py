@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.twl_abi_version() == 1
+    assert lib.twl_abi_version() == 2
 
 
 FAKE = 0x10000   # 16-byte aligned, never dereferenced: every call below fails host validation

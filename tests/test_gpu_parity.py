@@ -45,7 +45,7 @@ def _check_pack(twl, code, s_bits, label):
     announce(f"pack_ternary {label} N={code.shape[0]} K={code.shape[1]}")
     packed, q, smax = gpu_pack(twl, code, s_bits)
     op, oq, osm = O.pack_ternary(code, s_bits)
-    assert np.array_equal(host(packed), op), f"{label}: packed differs"
+    assert np.array_equal(host(packed).reshape(-1), op.reshape(-1)), f"{label}: packed differs"
     assert np.array_equal(host(q), oq), f"{label}: q differs"
     assert np.array_equal(host(smax).view(np.uint32), osm.view(np.uint32)), f"{label}: smax differs"
     return packed, q, smax, oq, osm
@@ -123,7 +123,8 @@ def test_stack_sampled_layers(twl):
             assert np.array_equal(host(q), oq), lbl0
             assert np.array_equal(host(smax).view(np.uint32), osm.view(np.uint32)), lbl0
             prow = rng.integers(0, N, 64)
-            assert np.array_equal(host(packed)[prow], O.pack_codes(code_h[prow])), lbl0
+            assert np.array_equal(O.untile_rows(host(packed), N, K)[prow],
+                                  O.pack_rows(code_h[prow])), lbl0
             xb = host(x_bits_d).view(np.uint16)
             for M in (512, 24):
                 lbl = f"stack L{layer} {name} M={M}"
@@ -194,7 +195,7 @@ def test_pack_edge_cases(twl):
     fixed = bad_code.copy()
     fixed[3, 5] = 0
     fixed[3, 900] = 0
-    assert np.array_equal(host(packed), O.pack_codes(fixed))
+    assert np.array_equal(host(packed).reshape(-1), O.pack_codes(fixed).reshape(-1))
 
 
 def test_empty_inputs(twl):

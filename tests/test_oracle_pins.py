@@ -218,15 +218,44 @@ def test_pack_worked_example():
     lines = dict(ln.split(":", 1) for ln in _golden_lines("pack_word.txt"))
     code = np.array([lines["codes"].split()], dtype=np.int8)
     want = [int(b, 16) for b in lines["bytes"].split()]
-    assert O.pack_codes(code)[0].tolist() == want
+    assert O.pack_rows(code)[0].tolist() == want
+
+
+def test_pack_tile_placement_worked_example():
+    # tests/golden/pack_tile.txt: byte offsets of three codes in the tiled
+    # buffer, worked by hand from the layout definition.
+    sets, expect, N, K, others = [], {}, 0, 0, None
+    for ln in _golden_lines("pack_tile.txt"):
+        key, val = ln.split(":", 1)
+        if key == "N":
+            N = int(val)
+        elif key == "K":
+            K = int(val)
+        elif key == "set":
+            sets.append(tuple(int(v) for v in val.split()))
+        elif key == "expect":
+            off, byte = val.split()
+            expect[int(off)] = int(byte, 16)
+        elif key == "others":
+            others = int(val, 16)
+    code = np.zeros((N, K), dtype=np.int8)
+    for n, k, c in sets:
+        code[n, k] = c
+    buf = O.pack_codes(code).reshape(-1)
+    assert buf.size == O.packed_bytes(N, K) == 8192
+    for i, b in enumerate(buf.tolist()):
+        assert b == expect.get(i, others), i
 
 
 def test_pack_roundtrip_and_size():
     layer = W.make_layer(13, 1, 2048, 33, codes="sparse40")
     p = O.pack_codes(layer.code)
-    assert p.shape == (33, 2048 // 4) and p.dtype == np.uint8
-    assert np.array_equal(O.unpack_codes(p, 2048), layer.code)
-    words = p.view("<u4")
+    assert p.shape == (1, 2048 // 128, 64, 32) and p.dtype == np.uint8
+    assert p.size == O.packed_bytes(33, 2048)
+    assert np.array_equal(O.unpack_codes(p, 33, 2048), layer.code)
+    assert np.array_equal(O.untile_rows(O.tile_rows(O.pack_rows(layer.code)), 33, 2048),
+                          O.pack_rows(layer.code))
+    words = p.reshape(-1).view("<u4")
     for i in range(16):                       # no 2-bit field holds 0b11
         assert not np.any(((words >> (2 * i)) & 3) == 3)
 
