@@ -112,10 +112,10 @@ size_t twl_packed_bytes(int64_t N, int64_t K);
 
 /*
  * Bytes of workspace twl_ternary_linear* may need for this shape on the
- * current device (0 = none; valid for every path).  The workspace holds the
- * GEMM's split-K partial tiles, or the GEMV's per-slice partial sums when it
- * splits K across workgroups; its contents on entry do not matter (no
- * clearing needed) and calls sharing a workspace must not run concurrently.
+ * current device (0 = none; valid for every path).  The workspace holds int32
+ * partial sums: the GEMM's split-K tiles, or the decode GEMV's per-slice sums
+ * when it splits K across workgroups.  Its contents on entry do not matter
+ * (no clearing needed); calls sharing a workspace must not run concurrently.
  */
 size_t twl_workspace_bytes(int64_t M, int64_t N, int64_t K);
 

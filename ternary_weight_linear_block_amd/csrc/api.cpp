@@ -177,11 +177,11 @@ twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const
   twl::DeviceInfo dev;
   TWL_TRY(current_device(&dev));
   const bool use_gemv = path == TWL_PATH_GEMV || (path == TWL_PATH_AUTO && M <= TWL_GEMV_MAX_M);
-  const size_t need = use_gemv ? twl::gemv_workspace_bytes(M, N, K, dev)
+  const size_t part = use_gemv ? twl::gemv_workspace_bytes(M, N, K, dev)
                                : twl::gemm_workspace_bytes(M, N, K, dev);
-  if (need > 0) {
-    if (workspace == nullptr || workspace_bytes < need)
-      return fail(TWL_EINVAL, "workspace of %zu bytes required (got %zu)", need,
+  if (part > 0) {
+    if (workspace == nullptr || workspace_bytes < part)
+      return fail(TWL_EINVAL, "workspace of %zu bytes required (got %zu)", part,
                   workspace == nullptr ? size_t{0} : workspace_bytes);
     if (!aligned16(workspace)) return fail(TWL_EALIGN, "workspace is not 16-byte aligned");
   }

@@ -11,10 +11,11 @@
 // bit-exact with the GEMM because both compute the same integer sum.
 //
 // gfx950 mapping
-//   * A wave owns 64 weight rows (lane l <-> row n0 + l) and one chunk of GPW
-//     consecutive 128-groups of K.  It issues the loads of its whole chunk up
-//     front (GPW x 2 KB per wave in flight), so the memory system sees the
-//     matrix as one burst instead of a latency-bound sequence of small reads.
+//   * A wave owns 64 weight rows (lane l <-> row n0 + l) and a run of at most
+//     GMAX consecutive 128-groups of K.  It issues the loads of its whole run
+//     up front (up to GMAX x 2 KB per wave in flight), so the memory system
+//     sees the matrix as one burst instead of a latency-bound sequence of
+//     small reads.
 //   * In the tiled weight layout a wave's group is one contiguous 2 KB tile,
 //     read with two 1 KB loads; one half-wave swap (v_permlane32_swap, 4 VALU
 //     operations per group) leaves each lane with its own row's 8 words; no
@@ -24,11 +25,12 @@
 //     loads, one copy in SGPRs per wave).
 //   * Per packed word: 1 shift, 4 ANDs, 4 byte-permutes against tables built
 //     from {-q, +q, 0}, then 4 v_dot4 per token.
-//   * A workgroup holds the waves of consecutive chunks of one 64-row block and
-//     adds their partial sums with LDS integer atomics (exact).  When there are
-//     too few row blocks to give every CU a workgroup, K is also split across
-//     workgroups ("slices"): each slice writes int32 partial sums to the
-//     workspace and a second kernel adds them in a fixed order and rescales.
+//   * A workgroup holds the waves of one 64-row block and one K range and adds
+//     their partial sums with LDS integer atomics (exact).  Streaming is
+//     bound per CU (about 22 GB/s each, measured), so every CU needs an equal
+//     share: when there are too few row blocks, K is also split across
+//     workgroups ("slices"), each slice writes its int32 partial sums to the
+//     workspace and a second kernel adds them in slice order and rescales.
 #include "twl_internal.h"
 
 #include <algorithm>
@@ -38,7 +40,7 @@
 namespace twl {
 namespace {
 
-constexpr int kMaxWaves = 8;
+constexpr int kMaxWaves = 16;
 
 // Activations are read at wave-uniform addresses; reading them through the
 // constant address space makes them scalar loads (one copy in SGPRs for the
@@ -84,7 +86,6 @@ struct GemvArgs {
   int32_t* part;      // [slices][M][N] int32 partial sums when slices > 1
   int N, K, G;        // G = K / 128
   int n_rb;           // 64-row blocks
-  int nch;            // chunks of GPW groups along K
   int slices;         // workgroups per row block (K split across workgroups)
   int out_acc;
 };
@@ -101,11 +102,12 @@ __device__ __forceinline__ void swap_halves(uint4& lo, uint4& hi) {
   hi = make_uint4(r0[1], r1[1], r2[1], r3[1]);
 }
 
-// MT is the exact number of tokens (1 .. 24); GPW the groups per wave chunk
-// (G is a multiple of 8, so every chunk is whole).  Static LDS: MT x 64 ints
-// for the cross-wave sums.
-template <int MT, int GPW>
-__global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
+// MT is the exact number of tokens (1 .. 24).  A workgroup of nw waves covers
+// one 64-row block and one K slice; its waves split the slice's groups as
+// evenly as possible, at most GMAX each.  Static LDS: MT x 64 ints for the
+// cross-wave sums.
+template <int MT, int GMAX>
+__global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a) {
   __shared__ int red[MT * 64];
   const int lane = threadIdx.x & 63;
   // wave index as a scalar: everything derived from it (the K range, the
@@ -120,12 +122,12 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
   for (int i = threadIdx.x; i < MT * 64; i += blockDim.x) red[i] = 0;
   __syncthreads();
 
-  const int c_lo = (slice * a.nch) / a.slices;
-  const int c_hi = ((slice + 1) * a.nch) / a.slices;
-  const int chunk = c_lo + wave;
+  const int s_lo = (slice * G) / a.slices;
+  const int s_n = ((slice + 1) * G) / a.slices - s_lo;
+  const int g0 = s_lo + (wave * s_n) / nw;
+  const int ng = s_lo + ((wave + 1) * s_n) / nw - g0;   // 0 .. GMAX
 
-  if (chunk < c_hi) {
-    const int g0 = chunk * GPW;
+  if (ng > 0) {
     // The group's weights are one contiguous 2 KB tile (64 rows x 32 bytes;
     // rows past N are code-0 padding), read with two 1 KB loads: in load A
     // lane l < 32 takes bytes 0-15 of row l and lane l >= 32 bytes 16-31 of
@@ -136,28 +138,20 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
     const int rlo = lane & 31;
     const uint8_t* srcA = a.packed + static_cast<size_t>(rb) * G * 2048 + rlo * 32 + hsel * 16;
     const uint8_t* srcB = srcA + 1024;
-    const int8_t* qrow = a.q + static_cast<size_t>(min(n0 + lane, N - 1)) * G + g0;
+    const int8_t* qrow = a.q + static_cast<size_t>(min(n0 + lane, N - 1)) * G;
 
-    // the whole chunk in flight at once
-    uint4 dA[GPW], dB[GPW];
+    // all of this wave's groups in flight at once (slots past ng re-read the
+    // last group, which is already on its way: no extra HBM traffic)
+    uint4 dA[GMAX], dB[GMAX];
 #pragma unroll
-    for (int j = 0; j < GPW; ++j) {
-      const size_t g = static_cast<size_t>(g0 + j);
+    for (int j = 0; j < GMAX; ++j) {
+      const size_t g = static_cast<size_t>(g0 + min(j, ng - 1));
       dA[j] = *reinterpret_cast<const uint4*>(srcA + g * 2048);
       dB[j] = *reinterpret_cast<const uint4*>(srcB + g * 2048);
     }
-    int8_t qv[GPW];
-    if (GPW == 8) {
-      const uint2 qq = *reinterpret_cast<const uint2*>(qrow);
+    int qv[GMAX];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) qv[j] = static_cast<int8_t>(qq.x >> (8 * j));
-#pragma unroll
-      for (int j = 4; j < GPW; ++j) qv[j] = static_cast<int8_t>(qq.y >> (8 * (j - 4)));
-    } else {
-      const uint32_t qq = *reinterpret_cast<const uint32_t*>(qrow);
-#pragma unroll
-      for (int j = 0; j < GPW; ++j) qv[j] = static_cast<int8_t>(qq >> (8 * j));
-    }
+    for (int j = 0; j < GMAX; ++j) qv[j] = qrow[g0 + min(j, ng - 1)];
 
     // small M: two accumulator chains per token so consecutive dot4s do not
     // wait on each other
@@ -169,7 +163,8 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
       for (int t = 0; t < MT; ++t) acc[c][t] = 0;
 
 #pragma unroll
-    for (int j = 0; j < GPW; ++j) {
+    for (int j = 0; j < GMAX; ++j) {
+      if (j != 0 && j >= ng) continue;   // ng >= 1: group 0 always runs
       uint4 lo = dA[j], hi = dB[j];
       swap_halves(lo, hi);
       const uint32_t words[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -203,20 +198,28 @@ __global__ __launch_bounds__(512) void gemv_kernel(GemvArgs a) {
   __syncthreads();
 
   const int n = n0 + lane;
-  if (n >= N) return;
-  for (int t = wave; t < MT; t += nw) {
-    const int s = red[t * 64 + lane];
-    if (a.slices > 1) {
-      a.part[(static_cast<size_t>(slice) * MT + t) * N + n] = s;
-    } else {
-      const size_t o = static_cast<size_t>(t) * N + n;
-      if (a.out_acc)
-        static_cast<int32_t*>(a.out)[o] = s;
-      else
-        static_cast<float*>(a.out)[o] =
-            static_cast<float>(s) * a.a_scale[t] * (a.smax[n] * (1.0f / 127.0f));
-    }
+  auto finish = [&](int t, int s) {
+    const size_t o = static_cast<size_t>(t) * N + n;
+    if (a.out_acc)
+      static_cast<int32_t*>(a.out)[o] = s;
+    else
+      static_cast<float*>(a.out)[o] =
+          static_cast<float>(s) * a.a_scale[t] * (a.smax[n] * (1.0f / 127.0f));
+  };
+  if (a.slices == 1) {
+    if (n < N)
+      for (int t = wave; t < MT; t += nw) finish(t, red[t * 64 + lane]);
+    return;
   }
+
+  // K is split across workgroups: this slice's partial sums go to the
+  // workspace; gemv_reduce_kernel adds the slices in order and rescales.  (A
+  // last-arriver scheme inside this kernel needs device-scope fences, which
+  // write back the L2 on this multi-XCD part and were measured to cost far
+  // more than the second launch.)
+  if (n < N)
+    for (int t = wave; t < MT; t += nw)
+      a.part[(static_cast<size_t>(slice) * MT + t) * N + n] = red[t * 64 + lane];
 }
 
 // Sum of the slices' partial sums in slice order, then the rescale.
@@ -242,30 +245,43 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const int32_t* __restr
 }
 
 struct GemvPlan {
-  int gpw = 8;     // groups per wave chunk (8 or 4)
+  int gmax = 2;    // compile-time bound on groups per wave
   int nw = 1;      // waves per workgroup
-  int slices = 1;  // workgroups per 64-row block
-  int nch = 1;     // chunks along K
+  int slices = 1;  // workgroups per 64-row block (K split across workgroups)
   int n_rb = 1;
 };
 
-GemvPlan make_plan(int64_t N, int64_t K, const DeviceInfo& dev) {
+constexpr int kGmaxChoices[] = {2, 3, 5, 9};
+
+// Streaming cost model (measured on MI355X): each CU moves about 22 GB/s, so
+// the busiest CU's bytes set the time; splitting K over several workgroups per
+// row block evens the CUs out but costs a second launch (about 3.5 us).
+constexpr double kCuBytesPerUs = 22.0e3;
+constexpr double kReduceUs = 3.5;
+
+GemvPlan make_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
   const int G = static_cast<int>(K >> 7);
-  const int n_rb = static_cast<int>((N + 63) / 64);
   const int cus = std::max(1, dev.cu_count);
   GemvPlan best;
-  for (int gpw : {8, 4}) {
+  double best_t = 1e30;
+  for (int slices = 1; slices <= 8 && slices <= G; ++slices) {
     GemvPlan p;
-    p.gpw = gpw;
-    p.n_rb = n_rb;
-    p.nch = G / gpw;   // G is a multiple of 8
-    // enough workgroups that every CU gets one, at most kMaxWaves waves each
-    p.slices = std::min(p.nch, std::max(1, (cus + n_rb - 1) / n_rb));
-    while ((p.nch + p.slices - 1) / p.slices > kMaxWaves) ++p.slices;
-    p.nw = (p.nch + p.slices - 1) / p.slices;
-    best = p;
-    // prefer the deeper chunk while it still leaves >= 4 waves per CU
-    if (static_cast<int64_t>(n_rb) * p.slices * p.nw >= 4 * static_cast<int64_t>(cus)) break;
+    p.n_rb = static_cast<int>((N + 63) / 64);
+    p.slices = slices;
+    const int per_slice = (G + slices - 1) / slices;
+    // two or three groups per wave keeps many waves in flight; at most 16
+    // waves, at most 9 groups each
+    p.nw = std::min(kMaxWaves, std::max(1, per_slice / 2));
+    const int gw = (per_slice + p.nw - 1) / p.nw;
+    if (gw > 9) continue;
+    for (int c : kGmaxChoices)
+      if (c >= gw) { p.gmax = c; break; }
+    const int64_t wgs = static_cast<int64_t>(p.n_rb) * slices;
+    const double per_cu = static_cast<double>((wgs + cus - 1) / cus) * 64.0 * per_slice * 32.0;
+    // partial sums: written once, read once by the reduce kernel (~4 TB/s)
+    const double part_us = slices > 1 ? 2.0 * slices * static_cast<double>(M) * N * 4 / 4.0e6 : 0.0;
+    const double t = per_cu / kCuBytesPerUs + (slices > 1 ? kReduceUs + part_us : 0.0);
+    if (t < best_t - 1e-9) { best_t = t; best = p; }
   }
   return best;
 }
@@ -274,10 +290,12 @@ template <int MT>
 hipError_t launch_mt(GemvArgs a, const GemvPlan& pl, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(pl.n_rb * pl.slices));
   const dim3 block(64 * pl.nw);
-  if (pl.gpw == 8)
-    hipLaunchKernelGGL((gemv_kernel<MT, 8>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((gemv_kernel<MT, 4>), grid, block, 0, stream, a);
+  switch (pl.gmax) {
+    case 2: hipLaunchKernelGGL((gemv_kernel<MT, 2>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((gemv_kernel<MT, 3>), grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((gemv_kernel<MT, 5>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((gemv_kernel<MT, 9>), grid, block, 0, stream, a); break;
+  }
   return hipGetLastError();
 }
 
@@ -285,23 +303,23 @@ hipError_t launch_mt(GemvArgs a, const GemvPlan& pl, hipStream_t stream) {
 
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  const GemvPlan pl = make_plan(N, K, dev);
+  const GemvPlan pl = make_plan(M, N, K, dev);
   if (pl.slices <= 1) return 0;
   return static_cast<size_t>(pl.slices) * static_cast<size_t>(M) * static_cast<size_t>(N) * 4;
 }
 
 hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
                        const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
-                       void* out, bool out_acc, void* workspace, size_t workspace_bytes,
+                       void* out, bool out_acc, void* part, size_t part_bytes,
                        const DeviceInfo& dev, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  const GemvPlan pl = make_plan(N, K, dev);
-  if (pl.slices > 1 && workspace_bytes < gemv_workspace_bytes(M, N, K, dev))
+  const GemvPlan pl = make_plan(M, N, K, dev);
+  if (pl.slices > 1 && (part == nullptr || part_bytes < gemv_workspace_bytes(M, N, K, dev)))
     return hipErrorInvalidValue;
   if (std::getenv("TWL_LOG"))
-    std::fprintf(stderr, "[twl] gemv M=%lld N=%lld K=%lld -> %d groups/wave, %d waves/WG, %d slices, grid=%d\n",
+    std::fprintf(stderr, "[twl] gemv M=%lld N=%lld K=%lld -> <= %d groups/wave, %d waves/WG, %d slices, grid=%d\n",
                  static_cast<long long>(M), static_cast<long long>(N), static_cast<long long>(K),
-                 pl.gpw, pl.nw, pl.slices, pl.n_rb * pl.slices);
+                 pl.gmax, pl.nw, pl.slices, pl.n_rb * pl.slices);
   GemvArgs a;
   a.x = x_i8;
   a.a_scale = a_scale;
@@ -309,12 +327,11 @@ hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* 
   a.q = q;
   a.smax = smax;
   a.out = out;
-  a.part = static_cast<int32_t*>(workspace);
+  a.part = static_cast<int32_t*>(part);
   a.N = static_cast<int>(N);
   a.K = static_cast<int>(K);
   a.G = static_cast<int>(K >> 7);
   a.n_rb = pl.n_rb;
-  a.nch = pl.nch;
   a.slices = pl.slices;
   a.out_acc = out_acc ? 1 : 0;
   hipError_t e = hipErrorInvalidValue;

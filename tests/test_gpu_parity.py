@@ -163,6 +163,30 @@ def test_gemv_vs_gemm_shapes(twl, M, N, K):
     assert np.array_equal(a1, a2)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 129, 32768), (5, 64, 65536), (24, 200, 20480)])
+def test_gemv_k_split_across_workgroups(twl, M, N, K):
+    # K large enough that the GEMV splits it over several workgroups per row
+    # block (partial sums in the workspace, added by a second kernel).
+    # Repeated calls on one workspace, interleaved with a GEMM call on it,
+    # must give identical results.
+    layer = W.make_layer(3000 + M + N, M, K, N, codes="sparse40")
+    x_i8, a_scale = O.rotate_quant_act(layer.x_bits, layer.sign)
+    packed, q, smax, oq, osm = _check_pack(twl, layer.code, layer.s_bits, "k-split")
+    oacc = O.linear_acc(x_i8, layer.code, oq)
+    oy = O.epilogue(oacc, a_scale, osm)
+    xi, sc = dev(x_i8), dev(a_scale)
+    ws = torch.full((max(1, twl.workspace_bytes(M, N, K)),), 0x5A, dtype=torch.uint8, device="cuda")
+    for rep in range(3):
+        announce(f"gemv k-split M={M} N={N} K={K} rep={rep}")
+        acc = host(twl.ternary_linear_acc(xi, packed, q, path=twl.PATH_GEMV, workspace=ws))
+        assert np.array_equal(acc, oacc), f"rep {rep}: acc differs"
+        y = host(twl.ternary_linear(xi, sc, packed, q, smax, path=twl.PATH_GEMV, workspace=ws))
+        np.testing.assert_allclose(y, oy, rtol=Y_RTOL, atol=0)
+        announce(f"gemm on the same workspace M={M} N={N} K={K} rep={rep}")
+        acc2 = host(twl.ternary_linear_acc(xi, packed, q, path=twl.PATH_GEMM, workspace=ws))
+        assert np.array_equal(acc2, oacc), f"rep {rep}: GEMM acc differs"
+
+
 def test_rotate_edge_cases(twl):
     # maximum width (64 blocks), one token
     layer = W.make_layer(31, 2, 65536, 1)
