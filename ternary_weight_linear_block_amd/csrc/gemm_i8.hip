@@ -72,6 +72,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Wait for this wave's outstanding LDS reads (and scalar loads).
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // Workgroup barrier without the memory fence __syncthreads implies: LDS
 // visibility is established by each wave's explicit vmcnt wait before it.
 __device__ __forceinline__ void bare_barrier() {
@@ -146,26 +149,32 @@ __device__ __forceinline__ v4i unpack16(uint32_t w, const QTables& t) {
 
 constexpr int kQTileBytes = 16384;  // q of a block tile: BN columns x its groups
 
-template <int RM, int FN>
+// Block tile of RM x FN fragments pairs (BM = 64 RM rows, BN = 32 FN columns)
+// computed by 4 WK waves: (wm, wn) split the tile 2 x 2 and, with WK = 2, a
+// pair of waves splits each stage's four k-steps.
+template <int RM, int FN, int WK>
 struct Tile {
   static constexpr int RN = (FN + 1) / 2;      // column fragments per wave
   static constexpr int BM = 64 * RM;
   static constexpr int BN = 32 * FN;
+  static constexpr int NW = 4 * WK;            // waves per workgroup
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int KS = 4 / WK;            // k-steps of a stage per wave
   static constexpr int STAGES = RM >= 4 ? 3 : kStages;
   static constexpr int A_BYTES = BM * kStageK; // x_i8 of one stage
   static constexpr int B_BYTES = BN * 32;      // BN columns x 2 half-planes x 16 B
   static constexpr int A_INSTR = A_BYTES / 1024;   // 1 KB per load instruction
   static constexpr int B_INSTR = B_BYTES / 1024;
-  static constexpr int A_PER_WAVE = (A_INSTR + 7) / 8;
-  static constexpr int B_PER_WAVE = (B_INSTR + 7) / 8;
+  static constexpr int A_PER_WAVE = (A_INSTR + NW - 1) / NW;
+  static constexpr int B_PER_WAVE = (B_INSTR + NW - 1) / NW;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int LOADS_PER_STAGE = A_PER_WAVE + B_PER_WAVE;
   static constexpr int SLOT_INTS = 4 * RM * RN * 64 * 16;  // one split's partial tile
   // wave-pair reduction: fragments exchanged per round through the LDS
   static constexpr int XCH_FRAGS = LDS_BYTES / (4 * 4096);
-  static_assert(XCH_FRAGS >= 1, "LDS too small for the wave-pair exchange");
-  static_assert(2 * LOADS_PER_STAGE < 64, "vmcnt range");
+  static_assert(WK == 1 || XCH_FRAGS >= 1, "LDS too small for the wave-pair exchange");
+  static_assert((STAGES - 1) * LOADS_PER_STAGE < 64, "vmcnt range");
 };
 
 struct GemmArgs {
@@ -198,7 +207,7 @@ __device__ __forceinline__ void store_tile(const v16i (&acc)[RM][(FN + 1) / 2], 
     const int cl = 32 * f + l32;
     const int col = n0 + cl;
     if (col >= N) continue;
-    const float cscale = OUT_ACC ? 0.0f : col_scale[cl];
+    const float cscale = OUT_ACC ? 0.0f : col_scale[cl] * (1.0f / 127.0f);
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
 #pragma unroll
@@ -238,24 +247,24 @@ __device__ __forceinline__ WorkItem work_item(int bid, int tiles_m, int tiles_n,
   return w;
 }
 
-template <int RM, int FN, bool OUT_ACC>
-__global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs p) {
-  using T = Tile<RM, FN>;
+template <int RM, int FN, int WK, bool OUT_ACC>
+__global__ __launch_bounds__(64 * 4 * WK, 1) void gemm_kernel(GemmArgs p) {
+  using T = Tile<RM, FN, WK>;
   constexpr int RN = T::RN, BN = T::BN;
   __shared__ __attribute__((aligned(1024))) int8_t smem[T::LDS_BYTES];
-  __shared__ __attribute__((aligned(16))) int8_t q_lds[kQTileBytes];
+  __shared__ __attribute__((aligned(16))) int8_t q_lds[kQTileBytes + 256];
   // epilogue scales of this tile, staged once: a_scale of its rows and
   // smax / 127 of its columns (reading them from global memory next to the
   // output stores would order every load behind the stores before it)
-  __shared__ float row_scale[T::BM];
-  __shared__ float col_scale[T::BN];
+  __shared__ __attribute__((aligned(16))) float row_scale[T::BM];
+  __shared__ __attribute__((aligned(16))) float col_scale[(T::BN + 63) / 64 * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1;
   const int wn = (wave >> 1) & 1;
-  const int wk = wave >> 2;  // which two k-steps of each stage
+  const int wk = WK == 1 ? 0 : wave >> 2;  // which k-steps of each stage
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
@@ -266,30 +275,41 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs p) {
   const int st_begin = w.split * p.stages_per_split;
   const int st_end = min(G, st_begin + p.stages_per_split);
 
-  // ---- once per tile: scales, and the q block [BN columns] x [groups g0 ..
-  // g0 + qw) (qw a multiple of 4; rows of q are contiguous, so this is a
-  // coalesced dword copy).  The planner keeps BN * qw <= kQTileBytes.
+  // ---- once per tile, loaded straight into LDS by the DMA path (no VGPR
+  // staging, so the compiler never waits on these loads): the q block
+  // [BN columns] x [groups g0 .. g0 + qw) (qw a multiple of 4, rows of q
+  // contiguous: dword copies), and the epilogue scales -- a_scale of the rows
+  // and smax of the columns.  Issued before the first stages' loads; the
+  // first pipeline wait covers them.  The planner keeps BN * qw <= kQTileBytes
+  // (q_lds has 256 spare bytes for the last, partly used instruction).
   const int g0 = st_begin & ~3;
   const int qw = (st_end - g0 + 3) & ~3;
   {
     const int qd = qw >> 2;
-    for (int idx = tid; idx < BN * qd; idx += 512) {
+    const int q_dwords = BN * qd;
+    const uint32_t q_base = lds_addr(q_lds);
+    const int8_t* q_tile = p.q + static_cast<size_t>(n0) * G;
+    for (int ii = wave; ii < (q_dwords + 63) / 64; ii += T::NW) {
+      const int idx = min(ii * 64 + lane, q_dwords - 1);
       const int c = idx / qd, d = idx - c * qd;
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(
-          p.q + static_cast<size_t>(min(n0 + c, N - 1)) * G + g0 + 4 * d);
-      *reinterpret_cast<uint32_t*>(q_lds + c * qw + 4 * d) = v;
+      dma4(sgpr_ptr(q_tile), static_cast<uint32_t>((min(n0 + c, N - 1) - n0) * G + g0 + 4 * d),
+           __builtin_amdgcn_readfirstlane(q_base + ii * 256));
     }
     if (!OUT_ACC) {
-      for (int r = tid; r < T::BM; r += 512) row_scale[r] = p.a_scale[min(m0 + r, M - 1)];
-      for (int c = tid; c < BN; c += 512) col_scale[c] = p.smax[min(n0 + c, N - 1)] * (1.0f / 127.0f);
+      const uint32_t r_base = lds_addr(row_scale), c_base = lds_addr(col_scale);
+      for (int ii = wave; ii < T::BM / 64; ii += T::NW)
+        dma4(sgpr_ptr(p.a_scale + m0), static_cast<uint32_t>((min(m0 + ii * 64 + lane, M - 1) - m0) * 4),
+             __builtin_amdgcn_readfirstlane(r_base + ii * 256));
+      for (int ii = wave; ii < (BN + 63) / 64; ii += T::NW)
+        dma4(sgpr_ptr(p.smax + n0), static_cast<uint32_t>((min(n0 + ii * 64 + lane, N - 1) - n0) * 4),
+             __builtin_amdgcn_readfirstlane(c_base + ii * 256));
     }
   }
-  __syncthreads();
 
   // ---- this wave's direct-to-LDS load slots.  Global addresses are a
   // wave-uniform tile base (SGPRs) plus a 32-bit per-lane offset; rows and
   // columns past M / N are clamped to the last one (computed, never stored).
-  // Load instructions are dealt round robin to the 8 waves; every wave issues
+  // Load instructions are dealt round robin to the waves; every wave issues
   // the same number per stage (a wave past the last instruction of a kind
   // repeats an earlier one: same data to the same LDS bytes), which keeps the
   // per-stage load count static for the vmcnt bookkeeping.
@@ -303,7 +323,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs p) {
   int a_lds[T::A_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < T::A_PER_WAVE; ++i) {
-    const int ia = (wave + 8 * i) % T::A_INSTR;
+    const int ia = (wave + T::NW * i) % T::A_INSTR;
     const int r = 8 * ia + (lane >> 3);
     const int chunk = (lane & 7) ^ chunk_swizzle(r);
     a_off[i] = static_cast<uint32_t>((min(m0 + r, M - 1) - m0) * K + 16 * chunk);
@@ -316,7 +336,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs p) {
   int b_lds[T::B_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < T::B_PER_WAVE; ++i) {
-    const int ib = (wave + 8 * i) % T::B_INSTR;
+    const int ib = (wave + T::NW * i) % T::B_INSTR;
     const int col = 32 * ib + (lane >> 1);
     const int h = (lane & 1) ^ ((col >> 3) & 1);
     const int nc = min(n0 + col, N - 1);
@@ -343,12 +363,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs p) {
   int a_row[RM];
 #pragma unroll
   for (int i = 0; i < RM; ++i) a_row[i] = wm * 32 * RM + 32 * i + l32;
-  int b_slot[RN];  // LDS byte offset of this lane's B data in a stage
+  int b_slot[RN];  // LDS byte offset of this lane's B words in a stage
   int q_pos[RN];   // offset of this lane's column in the q block
 #pragma unroll
   for (int j = 0; j < RN; ++j) {
     const int c = min(32 * (wn * RN + j) + l32, BN - 1);  // padding fragment clamped
-    b_slot[j] = (2 * c + (half ^ ((c >> 3) & 1))) * 16 + 8 * wk;
+    b_slot[j] = (2 * c + (half ^ ((c >> 3) & 1))) * 16 + 4 * T::KS * wk;
     q_pos[j] = c * qw - g0;
   }
 
@@ -358,55 +378,97 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < RN; ++j) acc[i][j] = v16i{0};
 
-  // ---- pipeline: stages st .. st + STAGES - 2 in flight while st is consumed
+  // ---- pipeline.  STAGES buffers, all in flight.  Per stage the wave runs KS
+  // k-steps (k-step index 4 wk / WK .. ), in two halves.  The operands of a
+  // stage are read from LDS ahead of the MFMAs that use them, so LDS latency
+  // hides behind matrix work: A of the second half while the first half's
+  // MFMAs run, and A of the next stage's first half, its packed words and q
+  // bytes (after the stage barrier) while the second half's MFMAs run.
+  // Loop body for stage st:
+  //   MFMAs(first half) | wait own DMA of st+1, barrier | read next stage |
+  //   MFMAs(second half) interleaved with the DMA of stage st+STAGES into the
+  //   buffer of st (free: the barrier proves every wave is past its reads).
+  constexpr int KS = T::KS, KH = KS / 2;
+  typedef unsigned int words_t __attribute__((ext_vector_type(KS)));
+  const int s0 = KS * wk;  // first k-step of this wave
+  const auto read_a = [&](int b, int h, v4i (&a)[RM][KH]) {
+    const int8_t* As = smem + b * T::STAGE_BYTES;
 #pragma unroll
-  for (int k = 0; k < T::STAGES - 1; ++k) issue(min(st_begin + k, st_end - 1), k);
-  int buf = 0;
-  for (int st = st_begin; st < st_end; ++st) {
-    wait_vmcnt<(T::STAGES - 2) * T::LOADS_PER_STAGE>();  // own loads of stage st done
-    bare_barrier();  // everyone's stage st is in LDS; everyone is done with stage st-1
-    const int nbuf = buf == 0 ? T::STAGES - 1 : buf - 1;  // (st + STAGES - 1) % STAGES
-    const int nst = min(st + T::STAGES - 1, st_end - 1);
-    // this stage's loads of stage nst are spread over the MFMA work below, so
-    // the address unit drains them while the matrix core is busy
-    constexpr int SLOTS = 2 * RN;
-
-    const int8_t* As = smem + buf * T::STAGE_BYTES;
-    const int8_t* Bs = As + T::A_BYTES;
-    uint2 bw[RN];  // this wave's two words (k-steps 2 wk, 2 wk + 1) per fragment
-    QTables tab[RN];
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+      for (int t = 0; t < KH; ++t)
+        a[i][t] = *reinterpret_cast<const v4i*>(
+            As + a_row[i] * kStageK + 16 * ((4 * half + s0 + KH * h + t) ^ chunk_swizzle(a_row[i])));
+  };
+  const auto read_b = [&](int b, int st, words_t (&bw)[RN], int (&qb)[RN]) {
+    const int8_t* Bs = smem + b * T::STAGE_BYTES + T::A_BYTES;
 #pragma unroll
     for (int j = 0; j < RN; ++j) {
-      bw[j] = *reinterpret_cast<const uint2*>(Bs + b_slot[j]);
-      tab[j] = make_tables(q_lds[q_pos[j] + st]);
+      bw[j] = *reinterpret_cast<const words_t*>(Bs + b_slot[j]);
+      qb[j] = q_lds[q_pos[j] + st];
     }
+  };
+  constexpr int S = T::STAGES;
+  constexpr int SLOTS = RN * KH;  // DMA issue slots in the second half
 #pragma unroll
-    for (int ss = 0; ss < 2; ++ss) {
-      const int s = 2 * wk + ss;
-      v4i a[RM];
+  for (int k = 0; k < S; ++k) issue(min(st_begin + k, st_end - 1), k);
+  wait_vmcnt<(S - 1) * T::LOADS_PER_STAGE>();  // own loads of the first stage done
+  bare_barrier();
+  v4i a0[RM][KH], a1[RM][KH];
+  words_t bw[RN];
+  int qb[RN];
+  read_a(0, 0, a0);
+  read_b(0, st_begin, bw, qb);
+  int buf = 0;
+  for (int st = st_begin; st < st_end; ++st) {
+    const int nbuf = buf == S - 1 ? 0 : buf + 1;
+    const int dst = min(st + S, st_end - 1);  // stage whose DMA reuses this buffer
+    QTables tab[RN];
 #pragma unroll
-      for (int i = 0; i < RM; ++i)
-        a[i] = *reinterpret_cast<const v4i*>(As + a_row[i] * kStageK +
-                                             16 * ((4 * half + s) ^ chunk_swizzle(a_row[i])));
+    for (int j = 0; j < RN; ++j) tab[j] = make_tables(qb[j]);
+    read_a(buf, 1, a1);
+    __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the first half's MFMAs
+    // first half
+#pragma unroll
+    for (int t = 0; t < KH; ++t)
 #pragma unroll
       for (int j = 0; j < RN; ++j) {
-        const v4i b = unpack16(ss == 0 ? bw[j].x : bw[j].y, tab[j]);
+        const v4i b = unpack16(bw[j][t], tab[j]);
 #pragma unroll
         for (int i = 0; i < RM; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b, acc[i][j], 0, 0, 0);
-        // load k of LOADS_PER_STAGE goes after MFMA group k * SLOTS / LOADS
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[i][t], b, acc[i][j], 0, 0, 0);
+      }
+    words_t bw1[RN];  // the second half's words: bw is refilled with the next stage below
+#pragma unroll
+    for (int j = 0; j < RN; ++j) bw1[j] = bw[j];
+    if (st + 1 < st_end) {
+      wait_lgkm0();  // this wave's reads of buffer `buf` have landed
+      wait_vmcnt<(S - 2) * T::LOADS_PER_STAGE>();  // own loads of stage st+1 done
+      bare_barrier();  // everyone's stage st+1 is in LDS; everyone is past buffer `buf`
+      read_a(nbuf, 0, a0);
+      read_b(nbuf, st + 1, bw, qb);
+      __builtin_amdgcn_sched_barrier(0);  // and these ahead of the second half's
+    }
+    // second half, with this stage's DMA into the freed buffer
+#pragma unroll
+    for (int t = 0; t < KH; ++t)
+#pragma unroll
+      for (int j = 0; j < RN; ++j) {
+        const v4i b = unpack16(bw1[j][KH + t], tab[j]);
+#pragma unroll
+        for (int i = 0; i < RM; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[i][t], b, acc[i][j], 0, 0, 0);
 #pragma unroll
         for (int k = 0; k < T::LOADS_PER_STAGE; ++k)
-          if ((k * SLOTS) / T::LOADS_PER_STAGE == ss * RN + j) issue_one(k, nst, nbuf);
+          if ((k * SLOTS) / T::LOADS_PER_STAGE == t * RN + j) issue_one(k, dst, buf);
       }
-    }
-    buf = buf == T::STAGES - 1 ? 0 : buf + 1;
+    buf = nbuf;
   }
   wait_vmcnt<0>();  // drain the padding loads of the tail before the LDS is reused
 
   // ---- add the wave pair's partials: wk = 1 hands its accumulators to wk = 0
   // through the (now idle) pipeline buffers, T::XCH_FRAGS fragments per round.
-  {
+  if (WK == 2) {
     constexpr int NF = RM * RN;
     int32_t* xch = reinterpret_cast<int32_t*>(smem);
     const int pair = wave & 3;
@@ -465,7 +527,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs p) {
 // (exact int32) and runs the same epilogue.
 template <int RM, int FN, bool OUT_ACC>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
-  using T = Tile<RM, FN>;
+  using T = Tile<RM, FN, 1>;
   constexpr int RN = T::RN;
   __shared__ float row_scale[T::BM];
   __shared__ float col_scale[T::BN];
@@ -475,7 +537,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
   const int m0 = (tile % p.tiles_m) * T::BM, n0 = (tile / p.tiles_m) * T::BN;
   if (!OUT_ACC) {
     for (int r = tid; r < T::BM; r += 256) row_scale[r] = p.a_scale[min(m0 + r, p.M - 1)];
-    for (int c = tid; c < T::BN; c += 256) col_scale[c] = p.smax[min(n0 + c, p.N - 1)] * (1.0f / 127.0f);
+    for (int c = tid; c < T::BN; c += 256) col_scale[c] = p.smax[min(n0 + c, p.N - 1)];
   }
   v16i acc[RM][RN];
 #pragma unroll
@@ -506,15 +568,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
 // ---------------------------------------------------------------- planner
 
 struct Plan {
-  int rm = 0, fn = 0, splits = 1, stages_per_split = 0, tiles_m = 0, tiles_n = 0;
+  int rm = 0, fn = 0, wk = 2, splits = 1, stages_per_split = 0, tiles_m = 0, tiles_n = 0;
   size_t slot_ints = 0;
 };
 
 struct Cfg {
-  int rm, fn;
+  int rm, fn, wk;
 };
-constexpr Cfg kCfgs[] = {{1, 4}, {1, 8}, {1, 10}, {2, 4}, {2, 5}, {2, 8},
-                         {2, 9}, {2, 10}, {4, 2}, {4, 4}};
+constexpr Cfg kCfgs[] = {{1, 4, 2}, {1, 8, 2}, {1, 10, 2}, {2, 4, 2}, {2, 5, 2},
+                         {2, 8, 2}, {2, 9, 2}, {2, 10, 2}, {4, 2, 2}, {4, 4, 2}};
 
 // Estimated cycles of one block tile on one CU.  Per 128-k stage and wave:
 // MFMA issue (32 cycles per 32x32x32, ~10% lost at one wave per SIMD), unpack
@@ -557,11 +619,18 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
       if (units > (int64_t{1} << 31) - 1) continue;
       if (static_cast<int64_t>(bn) * (((sps + 3) & ~3) + 4) > kQTileBytes) continue;
       const int64_t rounds = (units + cus - 1) / cus;
-      const double t = static_cast<double>(rounds) * tile_cycles(c.rm, c.fn, sps, splits);
+      const double tc = tile_cycles(c.rm, c.fn, sps, splits);
+      // makespan, plus a small charge for the total work (padding fragments,
+      // shared L2/HBM traffic) so that of two plans with the same number of
+      // rounds the one with fewer, fuller tiles wins
+      const double t = static_cast<double>(rounds) * tc +
+                       0.15 * tc * static_cast<double>(units) / cus *
+                           (static_cast<double>(2 * rn) / c.fn);
       if (t < best_t * 0.995) {
         best_t = t;
         best.rm = c.rm;
         best.fn = c.fn;
+        best.wk = c.wk;
         best.splits = splits;
         best.stages_per_split = sps;
         best.tiles_m = static_cast<int>(tm);
@@ -579,14 +648,15 @@ size_t plan_workspace_bytes(const Plan& pl) {
   return tiles * pl.splits * pl.slot_ints * sizeof(int32_t);
 }
 
-template <int RM, int FN>
+template <int RM, int FN, int WK>
 hipError_t launch_cfg(const GemmArgs& a, bool out_acc, hipStream_t stream) {
+  using T = Tile<RM, FN, WK>;
   const unsigned tiles = static_cast<unsigned>(a.tiles_m) * a.tiles_n;
   const unsigned grid = tiles * a.splits;
   if (out_acc)
-    hipLaunchKernelGGL((gemm_kernel<RM, FN, true>), dim3(grid), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<RM, FN, WK, true>), dim3(grid), dim3(T::THREADS), 0, stream, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<RM, FN, false>), dim3(grid), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<RM, FN, WK, false>), dim3(grid), dim3(T::THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits <= 1) return e;
   if (out_acc)
@@ -612,9 +682,9 @@ hipError_t launch_gemm(const int8_t* x_i8, const float* a_scale, const uint8_t* 
   if (pl.rm == 0 || 32 * pl.fn * (((pl.stages_per_split + 3) & ~3) + 4) > kQTileBytes)
     return hipErrorInvalidConfiguration;  // no plan fits the q block in LDS
   if (std::getenv("TWL_LOG"))
-    std::fprintf(stderr, "[twl] gemm M=%lld N=%lld K=%lld -> tile %dx%d splits=%d (%d groups each) grid=%d\n",
+    std::fprintf(stderr, "[twl] gemm M=%lld N=%lld K=%lld -> tile %dx%d, %d waves, splits=%d (%d groups each) grid=%d\n",
                  static_cast<long long>(M), static_cast<long long>(N), static_cast<long long>(K),
-                 64 * pl.rm, 32 * pl.fn, pl.splits, pl.stages_per_split,
+                 64 * pl.rm, 32 * pl.fn, 4 * pl.wk, pl.splits, pl.stages_per_split,
                  pl.tiles_m * pl.tiles_n * pl.splits);
   GemmArgs a;
   a.x = x_i8;
@@ -631,18 +701,18 @@ hipError_t launch_gemm(const int8_t* x_i8, const float* a_scale, const uint8_t* 
   a.tiles_n = pl.tiles_n;
   a.splits = pl.splits;
   a.stages_per_split = pl.stages_per_split;
-#define TWL_CFG(RM_, FN_) \
-  if (pl.rm == RM_ && pl.fn == FN_) return launch_cfg<RM_, FN_>(a, out_acc, stream);
-  TWL_CFG(1, 4)
-  TWL_CFG(1, 8)
-  TWL_CFG(1, 10)
-  TWL_CFG(2, 4)
-  TWL_CFG(2, 5)
-  TWL_CFG(2, 8)
-  TWL_CFG(2, 9)
-  TWL_CFG(2, 10)
-  TWL_CFG(4, 2)
-  TWL_CFG(4, 4)
+#define TWL_CFG(RM_, FN_, WK_) \
+  if (pl.rm == RM_ && pl.fn == FN_ && pl.wk == WK_) return launch_cfg<RM_, FN_, WK_>(a, out_acc, stream);
+  TWL_CFG(1, 4, 2)
+  TWL_CFG(1, 8, 2)
+  TWL_CFG(1, 10, 2)
+  TWL_CFG(2, 4, 2)
+  TWL_CFG(2, 5, 2)
+  TWL_CFG(2, 8, 2)
+  TWL_CFG(2, 9, 2)
+  TWL_CFG(2, 10, 2)
+  TWL_CFG(4, 2, 2)
+  TWL_CFG(4, 4, 2)
 #undef TWL_CFG
   return hipErrorInvalidValue;
 }

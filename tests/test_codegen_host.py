@@ -36,7 +36,7 @@ def asm(tmp_path_factory):
 def _kernels(asm_text):
     """name -> body for each gemm_kernel instantiation."""
     out = {}
-    for m in re.finditer(r"^(_Z\S*gemm_kernel\S*):[^\n]*\n(.*?)s_endpgm", asm_text, re.S | re.M):
+    for m in re.finditer(r"^(_Z\S*gemm_kernel\S*):[^\n]*\n(.*?)^\.Lfunc_end", asm_text, re.S | re.M):
         out[m.group(1)] = m.group(2)
     assert len(out) >= 10, f"expected every gemm_kernel instantiation, found {len(out)}"
     return out
@@ -57,17 +57,39 @@ def test_m0_only_feeds_our_lds_loads(asm):
                 pytest.fail(f"{name}: compiler-generated use of m0: {ln}")
 
 
+def _loops(body):
+    """Innermost loops of a kernel body as text: the header block plus every
+    block the compiler annotates as belonging to it (rotated loops put blocks
+    before the header), each block running to the next label."""
+    lines = body.splitlines()
+    label_re = re.compile(r"^(\.LBB\w+|; %bb\.\d+):")
+    blocks, cur = [], None
+    for ln in lines:
+        m = label_re.match(ln.strip())
+        if m:
+            cur = [ln]
+            blocks.append(cur)
+        elif cur is not None:
+            cur.append(ln)
+    loops = {}
+    for b in blocks:
+        head = b[0]
+        m = re.search(r"Header=(BB\w+)", head)
+        if "Inner Loop Header" in head:
+            key = head.split(":")[0].strip()[2:]   # ".LBBn_m" -> "BBn_m"
+        elif m:
+            key = m.group(1)
+        else:
+            continue
+        loops.setdefault(key, []).append("\n".join(b))
+    return {k: "\n".join(v) for k, v in loops.items()}
+
+
 def test_main_loop_has_one_wait_and_no_accumulator_copies(asm):
     for name, body in _kernels(asm).items():
-        lines = body.splitlines()
-        loop = None
-        for head in [i for i, ln in enumerate(lines) if "Loop Header" in ln]:
-            end = next(i for i in range(head, len(lines)) if "s_cbranch_scc" in lines[i])
-            cand = "\n".join(lines[head:end + 1])
-            if "v_mfma" in cand:
-                loop = cand
-                break
-        assert loop is not None, name
+        mains = [t for t in _loops(body).values() if "v_mfma" in t]
+        assert len(mains) == 1, (name, len(mains))
+        loop = mains[0]
         assert loop.count("vmcnt") == 1, name
         assert "v_accvgpr" not in loop, name
         assert "v_mfma_i32_32x32x32_i8" in loop, name
