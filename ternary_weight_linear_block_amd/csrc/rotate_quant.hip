@@ -9,19 +9,24 @@
 // H1024 [a; b] = [H512 a + H512 b ; H512 a - H512 b], i.e. the last butterfly
 // stage combines the two 512-halves, so stages run h = 1, 2, ..., 512.
 //
-// Layout on the GPU: one workgroup per token.  Wave w owns the 1024-blocks
-// w, w + nw, ... of the row; lane l holds the 16 contiguous elements
-// 16l .. 16l+15 of each block in registers.  Stages h = 1..8 are in-lane,
-// stages h = 16..512 pair lane l with lane l ^ (h/16) through cross-lane
-// shuffles.  The per-token absmax is reduced across lanes and waves, then each
-// lane quantises its registers and writes 16 bytes.  The input is read once
-// and the output written once: the kernel is bound by HBM traffic
-// (2 B in + 1 B out per element).
+// Layout on the GPU: one workgroup per token; wave w owns the 1024-blocks
+// w, w + nw, ... of the row.  A block lives in registers, 16 elements per
+// lane, and every butterfly runs inside a lane: the element index e (10 bits)
+// is split between lane and register slot three times, with two LDS
+// transposes in between (per-wave buffer, padded to be bank-conflict free):
+//   layout 0: lane = e[9:4],            slot = e[3:0]  -> stages h = 1 .. 8
+//   layout 1: lane = e[9:8] e[3:0],     slot = e[7:4]  -> stages h = 16 .. 128
+//   layout 2: lane = e[7:2],            slot = e[9:8] e[1:0] -> stages h = 256, 512
+// so the pass has no cross-lane arithmetic at all.  In layout 2 a lane holds
+// four runs of 4 consecutive elements, which it quantises and stores as four
+// dwords (each store instruction writes 256 contiguous bytes).  The
+// per-token absmax is reduced across lanes and waves.  The input is read once
+// and the output written once: 2 B in + 1 B out per element.
 //
 // Every butterfly is (lo, hi) -> (lo + hi, lo - hi) in fp32 with the same
-// operands as a textbook in-place FWHT, so the result is bit-identical to any
-// implementation that follows the same stage order; the build uses
-// -ffp-contract=off so no add is fused with anything.
+// operands as a textbook in-place FWHT and in the same stage order, so the
+// result is bit-identical to any implementation that follows that order; the
+// build uses -ffp-contract=off so no add is fused with anything.
 #include "twl_internal.h"
 
 namespace twl {
@@ -33,41 +38,51 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// Stages h = 1, 2, 4, 8 inside one lane's 16 consecutive elements.
-__device__ __forceinline__ void fwht16_in_lane(float (&v)[16]) {
+// The butterflies of stage h = 2^b on register slot bit `sb` of a 16-slot
+// lane: slot j (bit sb clear) holds the lower position, j | (1 << sb) the
+// upper one.
+__device__ __forceinline__ void stage_in_lane(float (&v)[16], int sb) {
+  const int m = 1 << sb;
 #pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if ((j & h) == 0) {
-        const float lo = v[j];
-        const float hi = v[j + h];
-        v[j] = lo + hi;
-        v[j + h] = lo - hi;
-      }
+  for (int j = 0; j < 16; ++j) {
+    if ((j & m) == 0) {
+      const float lo = v[j];
+      const float hi = v[j + m];
+      v[j] = lo + hi;
+      v[j + m] = lo - hi;
     }
   }
 }
 
-// One cross-lane stage: the partner lane is lane ^ mask.  The lane whose mask
-// bit is clear holds the lower position (lo), its partner the upper one (hi).
-__device__ __forceinline__ void fwht_cross_stage(float (&v)[16], int mask, bool upper) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const float p = __shfl_xor(v[j], mask);
-    v[j] = upper ? (p - v[j]) : (v[j] + p);
-  }
+// LDS word addresses of element e in the two transposes (padded so that both
+// the writes and the reads of each transpose hit 64 distinct banks).
+__device__ __forceinline__ int addr_a(int e) { return (e >> 4) * 20 + (e & 15) + 16 * (e >> 8); }
+__device__ __forceinline__ int addr_b(int e) { return e + 16 * (e >> 8); }
+constexpr int kWaveBufWords = 1344;  // > max addr_a (1323) and addr_b (1071)
+
+__device__ __forceinline__ void lds_wave_sync() {
+  // LDS operations of one wave execute in order; the fences only keep the
+  // compiler from moving reads above the writes they depend on (or the next
+  // writes above these reads)
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int BPW>
 __global__ __launch_bounds__(1024) void rotate_quant_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ sign, int K, int nblocks,
     int8_t* __restrict__ x_i8, float* __restrict__ a_scale) {
+  extern __shared__ float wbuf_all[];  // nw x kWaveBufWords
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
   const uint16_t* xr = x + static_cast<size_t>(t) * K;
+  float* wb = wbuf_all + wave * kWaveBufWords;
+  // layout-1 lane bits: e[9:8] = lane >> 4, e[3:0] = lane & 15;
+  // layout-2 lane bits: e[7:2] = lane
+  const int l1_hi = lane >> 4, l1_lo = lane & 15;
 
   float v[BPW][16];
   float amax = 0.0f;
@@ -76,26 +91,56 @@ __global__ __launch_bounds__(1024) void rotate_quant_kernel(
   for (int i = 0; i < BPW; ++i) {
     const int b = wave + i * nw;
     if (b < nblocks) {
+      // layout 0: element e = 16 lane + slot
       const int k0 = b * kBlock + lane * 16;
       const uint4 p0 = *reinterpret_cast<const uint4*>(xr + k0);
       const uint4 p1 = *reinterpret_cast<const uint4*>(xr + k0 + 8);
       const uint4 sg = *reinterpret_cast<const uint4*>(sign + k0);
       const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
       const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
+      float(&w)[16] = v[i];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const uint32_t bits = (pw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
         // multiply by the +-1 sign: flip the fp32 sign bit when the int8 sign is negative
         const uint32_t flip = ((sw[e >> 2] >> (8 * (e & 3) + 7)) & 1u) << 31;
-        v[i][e] = __uint_as_float(__float_as_uint(bf16_bits_to_float(bits)) ^ flip);
+        w[e] = __uint_as_float(__float_as_uint(bf16_bits_to_float(bits)) ^ flip);
       }
-      fwht16_in_lane(v[i]);
 #pragma unroll
-      for (int m = 1; m < 64; m <<= 1) fwht_cross_stage(v[i], m, (lane & m) != 0);
+      for (int sb = 0; sb < 4; ++sb) stage_in_lane(w, sb);  // h = 1, 2, 4, 8
+
+      // transpose to layout 1: slot s holds e = 256 l1_hi + 16 s + l1_lo
+      lds_wave_sync();
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(wb + addr_a(16 * lane + 4 * q)) =
+            make_float4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+      lds_wave_sync();
+#pragma unroll
+      for (int sl = 0; sl < 16; ++sl) w[sl] = wb[addr_a(256 * l1_hi + 16 * sl + l1_lo)];
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) stage_in_lane(w, sb);  // h = 16, 32, 64, 128
+
+      // transpose to layout 2: slot 4 c + d holds e = 256 c + 4 lane + d
+      lds_wave_sync();
+#pragma unroll
+      for (int sl = 0; sl < 16; ++sl) wb[addr_b(256 * l1_hi + 16 * sl + l1_lo)] = w[sl];
+      lds_wave_sync();
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 f = *reinterpret_cast<const float4*>(wb + addr_b(256 * c + 4 * lane));
+        w[4 * c] = f.x;
+        w[4 * c + 1] = f.y;
+        w[4 * c + 2] = f.z;
+        w[4 * c + 3] = f.w;
+      }
+#pragma unroll
+      for (int sb = 2; sb < 4; ++sb) stage_in_lane(w, sb);  // h = 256, 512
+
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        v[i][e] *= 0.03125f;  // orthonormal 1/sqrt(1024): exact power of two
-        amax = fmaxf(amax, fabsf(v[i][e]));
+        w[e] *= 0.03125f;  // orthonormal 1/sqrt(1024): exact power of two
+        amax = fmaxf(amax, fabsf(w[e]));
       }
     }
   }
@@ -111,24 +156,27 @@ __global__ __launch_bounds__(1024) void rotate_quant_kernel(
   const float scale = tmax / 127.0f;  // IEEE division
   if (threadIdx.x == 0) a_scale[t] = scale;
 
+  // a zero scale (all-zero row, or an absmax so small that absmax / 127
+  // underflows) quantises every element to 0: dividing by 1 instead gives
+  // rint(|v| <= tiny) = 0 without a branch per element
+  const float div = scale > 0.0f ? scale : 1.0f;
   int8_t* yr = x_i8 + static_cast<size_t>(t) * K;
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
     const int b = wave + i * nw;
     if (b < nblocks) {
-      uint32_t packedq[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        int qv = 0;
-        if (scale > 0.0f) {
-          float r = rintf(v[i][e] / scale);  // IEEE division, ties to even
+      for (int c = 0; c < 4; ++c) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          float r = rintf(v[i][4 * c + d] / div);  // IEEE division, ties to even
           r = fminf(fmaxf(r, -127.0f), 127.0f);
-          qv = static_cast<int>(r);
+          const int qv = static_cast<int>(r);
+          word |= (static_cast<uint32_t>(qv) & 0xFFu) << (8 * d);
         }
-        packedq[e >> 2] |= (static_cast<uint32_t>(qv) & 0xFFu) << (8 * (e & 3));
+        *reinterpret_cast<uint32_t*>(yr + b * kBlock + 256 * c + 4 * lane) = word;
       }
-      *reinterpret_cast<uint4*>(yr + b * kBlock + lane * 16) =
-          make_uint4(packedq[0], packedq[1], packedq[2], packedq[3]);
     }
   }
 }
@@ -138,8 +186,17 @@ hipError_t launch_bpw(const uint16_t* x, const int8_t* sign, int64_t M, int64_t 
                       int8_t* x_i8, float* a_scale, hipStream_t stream) {
   const int nblocks = static_cast<int>(K / kBlock);
   const int nw = (nblocks + BPW - 1) / BPW;
-  hipLaunchKernelGGL(rotate_quant_kernel<BPW>, dim3(static_cast<unsigned>(M)), dim3(64 * nw), 0,
-                     stream, x, sign, static_cast<int>(K), nblocks, x_i8, a_scale);
+  const size_t lds = static_cast<size_t>(nw) * kWaveBufWords * sizeof(float);
+  if (lds > 65536) {
+    // more than the default dynamic LDS limit: the part has 160 KiB per CU
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(rotate_quant_kernel<BPW>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(rotate_quant_kernel<BPW>, dim3(static_cast<unsigned>(M)), dim3(64 * nw),
+                     lds, stream, x, sign,
+                     static_cast<int>(K), nblocks, x_i8, a_scale);
   return hipGetLastError();
 }
 
