@@ -57,9 +57,11 @@ typedef enum {
 
 /* Which kernel family computes the linear layer (twl_ternary_linear_ex). */
 typedef enum {
-  TWL_PATH_AUTO = 0,     /* GEMV for M <= TWL_GEMV_MAX_M, else the MFMA GEMM */
-  TWL_PATH_GEMM = 1,     /* int8-MFMA GEMM with in-register 2-bit unpack     */
-  TWL_PATH_GEMV = 2      /* packed-2-bit dot4 GEMV (M <= TWL_GEMV_MAX_M)     */
+  TWL_PATH_AUTO = 0,       /* decode kernel for M <= TWL_GEMV_MAX_M, else the GEMM */
+  TWL_PATH_GEMM = 1,       /* int8-MFMA GEMM with in-register 2-bit unpack         */
+  TWL_PATH_GEMV = 2,       /* decode kernel (M <= TWL_GEMV_MAX_M), chosen by M     */
+  TWL_PATH_GEMV_DOT4 = 3,  /* decode: packed-2-bit dot4 GEMV, no matrix cores      */
+  TWL_PATH_GEMV_MFMA = 4   /* decode: 32-token-padded int8 MFMA over the stream    */
 } twl_path;
 
 /*
@@ -146,7 +148,9 @@ twl_status twl_ternary_linear_acc(const int8_t* x_i8, const uint8_t* packed, con
 /*
  * ternary_linear_ex -- explicit kernel family.  out_acc != 0 writes int32 acc
  * into `out` (a_scale and smax are then ignored and may be NULL), otherwise fp32
- * y.  TWL_PATH_GEMV requires M <= TWL_GEMV_MAX_M.
+ * y.  The decode paths (TWL_PATH_GEMV, _GEMV_DOT4, _GEMV_MFMA) require
+ * M <= TWL_GEMV_MAX_M; TWL_PATH_GEMV picks the dot4 kernel for the smallest
+ * batches and the MFMA kernel above.  All paths give bit-identical acc.
  */
 twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
                                  const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,

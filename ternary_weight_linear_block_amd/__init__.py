@@ -16,11 +16,13 @@ from __future__ import annotations
 from typing import Optional, Tuple
 
 from . import _lib
-from ._lib import GEMV_MAX_M, GROUP, HBLOCK, MAX_K, PATH_AUTO, PATH_GEMM, PATH_GEMV, TwlError
+from ._lib import (GEMV_MAX_M, GROUP, HBLOCK, MAX_K, PATH_AUTO, PATH_GEMM, PATH_GEMV, PATH_GEMV_DOT4,
+                   PATH_GEMV_MFMA, TwlError)
 
 __all__ = [
     "rotate_quant_act", "pack_ternary", "ternary_linear", "ternary_linear_acc",
-    "workspace_bytes", "packed_bytes", "TwlError", "PATH_AUTO", "PATH_GEMM", "PATH_GEMV", "GEMV_MAX_M",
+    "workspace_bytes", "packed_bytes", "TwlError", "PATH_AUTO", "PATH_GEMM", "PATH_GEMV", "PATH_GEMV_DOT4",
+    "PATH_GEMV_MFMA", "GEMV_MAX_M",
     "HBLOCK", "GROUP", "MAX_K", "library",
 ]
 

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libtwl.so")
 TWL_OK = 0
 STATUS_NAMES = {0: "TWL_OK", 1: "TWL_EINVAL", 2: "TWL_ESHAPE", 3: "TWL_EALIGN",
                 4: "TWL_EDEVICE", 5: "TWL_EHIP"}
-PATH_AUTO, PATH_GEMM, PATH_GEMV = 0, 1, 2
+PATH_AUTO, PATH_GEMM, PATH_GEMV, PATH_GEMV_DOT4, PATH_GEMV_MFMA = 0, 1, 2, 3, 4
 HBLOCK, GROUP, MAX_K, GEMV_MAX_M = 1024, 128, 65536, 24
 
 # (name, restype, argtypes) for every symbol include/twl.h declares

@@ -149,7 +149,9 @@ size_t twl_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   // the GEMM's need, also for M <= TWL_GEMV_MAX_M (TWL_PATH_GEMM may be forced),
   // and the GEMV's where that path may run
   size_t need = twl::gemm_workspace_bytes(M, N, K, dev);
-  if (M <= TWL_GEMV_MAX_M) need = std::max(need, twl::gemv_workspace_bytes(M, N, K, dev));
+  if (M <= TWL_GEMV_MAX_M)
+    for (twl::GemvKind kind : {twl::kGemvAuto, twl::kGemvDot4, twl::kGemvMfma})
+      need = std::max(need, twl::gemv_workspace_bytes(M, N, K, kind, dev));
   return need;
 }
 
@@ -160,10 +162,11 @@ twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const
   TWL_TRY(check_rows("M", M));
   TWL_TRY(check_rows("N", N));
   TWL_TRY(check_k(K));
-  if (path != TWL_PATH_AUTO && path != TWL_PATH_GEMM && path != TWL_PATH_GEMV)
+  if (path < TWL_PATH_AUTO || path > TWL_PATH_GEMV_MFMA)
     return fail(TWL_EINVAL, "unknown path %d", path);
-  if (path == TWL_PATH_GEMV && M > TWL_GEMV_MAX_M)
-    return fail(TWL_ESHAPE, "the GEMV path takes M <= %d (got %lld)", TWL_GEMV_MAX_M,
+  const bool decode_path = path >= TWL_PATH_GEMV;
+  if (decode_path && M > TWL_GEMV_MAX_M)
+    return fail(TWL_ESHAPE, "the decode paths take M <= %d (got %lld)", TWL_GEMV_MAX_M,
                 static_cast<long long>(M));
   if (M == 0 || N == 0) return ok();
   TWL_REQUIRE_PTR(x_i8);
@@ -176,8 +179,11 @@ twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const
   }
   twl::DeviceInfo dev;
   TWL_TRY(current_device(&dev));
-  const bool use_gemv = path == TWL_PATH_GEMV || (path == TWL_PATH_AUTO && M <= TWL_GEMV_MAX_M);
-  const size_t part = use_gemv ? twl::gemv_workspace_bytes(M, N, K, dev)
+  const bool use_gemv = decode_path || (path == TWL_PATH_AUTO && M <= TWL_GEMV_MAX_M);
+  const twl::GemvKind kind = path == TWL_PATH_GEMV_DOT4   ? twl::kGemvDot4
+                             : path == TWL_PATH_GEMV_MFMA ? twl::kGemvMfma
+                                                          : twl::kGemvAuto;
+  const size_t part = use_gemv ? twl::gemv_workspace_bytes(M, N, K, kind, dev)
                                : twl::gemm_workspace_bytes(M, N, K, dev);
   if (part > 0) {
     if (workspace == nullptr || workspace_bytes < part)
@@ -187,7 +193,7 @@ twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const
   }
   if (use_gemv)
     return launched(twl::launch_gemv(x_i8, a_scale, packed, q, smax, M, N, K, out, out_acc != 0,
-                                     workspace, workspace_bytes, dev, stream),
+                                     workspace, workspace_bytes, kind, dev, stream),
                     "ternary_linear (GEMV)");
   return launched(twl::launch_gemm(x_i8, a_scale, packed, q, smax, M, N, K, out, out_acc != 0,
                                    workspace, workspace_bytes, dev, stream),

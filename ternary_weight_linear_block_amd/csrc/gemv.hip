@@ -1,5 +1,6 @@
-// Decode ternary linear (M <= 24 tokens): an HBM-streaming GEMV over the
-// packed 2-bit weights using the VALU int8 dot product (v_dot4), no MFMA.
+// Decode ternary linear (M <= 24 tokens): two HBM-streaming kernels over the
+// packed 2-bit weights, a VALU int8 dot-product GEMV for the smallest batches
+// and a matrix-core variant for the rest.
 //
 // Method ([P1] "Ternary-Bonsai-2-27B on 2x RTX 5070 with vLLM TP=2", section 4
 // for the arithmetic, section 5 for the prior art): the same exact int32
@@ -7,30 +8,31 @@
 //   acc[t,n] = sum_k x_i8[t,k] * code[n,k] * q[n, k/128],
 //   y[t,n]   = acc[t,n] * a_scale[t] * smax[n] / 127.
 // The pages tried a dp4a decode GEMV on their GPU (section 5 table: 2.1x as a
-// kernel, +2% end to end, rejected because its error grew); here the GEMV is
-// bit-exact with the GEMM because both compute the same integer sum.
+// kernel, +2% end to end, rejected because its error grew); here both decode
+// kernels are bit-exact with the GEMM because all compute the same integer sum.
 //
-// gfx950 mapping
-//   * A wave owns 64 weight rows (lane l <-> row n0 + l) and a run of at most
-//     GMAX consecutive 128-groups of K.  It issues the loads of its whole run
-//     up front (up to GMAX x 2 KB per wave in flight), so the memory system
-//     sees the matrix as one burst instead of a latency-bound sequence of
-//     small reads.
-//   * In the tiled weight layout a wave's group is one contiguous 2 KB tile,
-//     read with two 1 KB loads; one half-wave swap (v_permlane32_swap, 4 VALU
-//     operations per group) leaves each lane with its own row's 8 words; no
-//     LDS round trip in the loop.
-//   * The activations of a group are the same for all 64 rows: they are read
-//     at wave-uniform addresses through the constant address space (scalar
-//     loads, one copy in SGPRs per wave).
+// gfx950 mapping (both kernels)
+//   * A workgroup holds one 64-row block and one K range; each wave takes a
+//     run of at most GMAX consecutive 128-groups of that range and issues the
+//     loads of its whole run up front (up to GMAX x 2 KB per wave in flight),
+//     so the memory system sees the matrix as one burst instead of a
+//     latency-bound sequence of small reads.  In the tiled weight layout a
+//     wave's group is one contiguous 2 KB tile, read with two 1 KB loads.
 //   * Per packed word: 1 shift, 4 ANDs, 4 byte-permutes against tables built
-//     from {-q, +q, 0}, then 4 v_dot4 per token.
-//   * A workgroup holds the waves of one 64-row block and one K range and adds
-//     their partial sums with LDS integer atomics (exact).  Streaming is
-//     bound per CU (about 22 GB/s each, measured), so every CU needs an equal
-//     share: when there are too few row blocks, K is also split across
-//     workgroups ("slices"), each slice writes its int32 partial sums to the
-//     workspace and a second kernel adds them in slice order and rescales.
+//     from {-q, +q, 0} give the 16 int8 weights code * q.
+//   * The waves' partial sums meet in LDS through integer atomics (exact).
+//     Streaming is bound per CU (about 22 GB/s each, measured), so every CU
+//     needs an equal share: when there are too few row blocks, K is also split
+//     across workgroups ("slices"), each slice writes its int32 partial sums to
+//     the workspace and a second kernel adds them in slice order and rescales.
+// dot4 kernel (gemv_kernel): lane l owns row n0 + l; one half-wave swap
+//   (v_permlane32_swap) gives each lane its row's 8 words, then 4 v_dot4 per
+//   word and token, with the activations read at wave-uniform addresses
+//   through the constant address space (scalar loads, one copy per wave).
+//   Its VALU work grows with M: it is used for M < 4.
+// MFMA kernel (gemv_mfma_kernel): the tokens padded to 32 form the B operand
+//   of v_mfma_i32_32x32x32_i8 and the unpacked weights the A operand; the
+//   matrix cores make the work nearly independent of M (see the kernel).
 #include "twl_internal.h"
 
 #include <algorithm>
@@ -222,6 +224,107 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a) {
       a.part[(static_cast<size_t>(slice) * MT + t) * N + n] = red[t * 64 + lane];
 }
 
+// Decode with the matrix cores (M = 2 .. 32 tokens, padded to 32).  Same
+// work split as gemv_kernel (one 64-row block and one K slice per workgroup,
+// a run of at most GMAX groups per wave), but each group is 8 MFMAs
+// v_mfma_i32_32x32x32_i8: A = the unpacked weights of 32 rows x 32 k
+// (subtile s = rows 32 s .. 32 s + 31 of the block, k-step t), B = 32 k x 32
+// tokens of x_i8.  The k values of a (lane half h, k-step t) pair only have to
+// agree between A and B: lane half h at k-step t covers k = 16 (4 h + t) ..
+// +15 of the group, so a lane's weights for the whole group are the 16
+// contiguous packed bytes [16 h, 16 h + 16) of its row (one load per subtile,
+// no lane exchange), and its activations are the 64 contiguous bytes
+// [64 h, 64 h + 64) of token row j of the group.  Columns j >= M re-read row
+// M - 1 and are never reduced.
+constexpr int kRedStride = 40;  // [n][m] int32 sums: 64 rows, 32 tokens, padded
+
+template <int GMAX, int MAXT>
+__global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(GemvArgs a, int M) {
+  __shared__ int red[64 * kRedStride];
+  typedef int v16i __attribute__((ext_vector_type(16)));
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const int rb = blockIdx.x % a.n_rb;
+  const int slice = blockIdx.x / a.n_rb;
+  const int n0 = rb * 64;
+  const int N = a.N, K = a.K, G = a.G;
+
+  for (int i = threadIdx.x; i < 64 * kRedStride; i += blockDim.x) red[i] = 0;
+  __syncthreads();
+
+  const int s_lo = (slice * G) / a.slices;
+  const int s_n = ((slice + 1) * G) / a.slices - s_lo;
+  const int g0 = s_lo + (wave * s_n) / nw;
+  const int ng = s_lo + ((wave + 1) * s_n) / nw - g0;   // 0 .. GMAX
+
+  if (ng > 0) {
+    const int j = lane & 31;   // A: weight row in the subtile; B: token column
+    const int h = lane >> 5;   // lane half
+    const uint8_t* srcA = a.packed + static_cast<size_t>(rb) * G * 2048 + j * 32 + h * 16;
+    const uint8_t* srcB = srcA + 1024;
+    const int8_t* qrowA = a.q + static_cast<size_t>(min(n0 + j, N - 1)) * G;
+    const int8_t* qrowB = a.q + static_cast<size_t>(min(n0 + 32 + j, N - 1)) * G;
+    const int8_t* xrow = a.x + static_cast<size_t>(min(j, M - 1)) * K + h * 64;
+
+    uint4 dA[GMAX], dB[GMAX];
+    v4i xv[GMAX][4];
+#pragma unroll
+    for (int jj = 0; jj < GMAX; ++jj) {
+      const size_t g = static_cast<size_t>(g0 + min(jj, ng - 1));
+      dA[jj] = *reinterpret_cast<const uint4*>(srcA + g * 2048);
+      dB[jj] = *reinterpret_cast<const uint4*>(srcB + g * 2048);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) xv[jj][t] = *reinterpret_cast<const v4i*>(xrow + g * 128 + 16 * t);
+    }
+    int qa[GMAX], qb[GMAX];
+#pragma unroll
+    for (int jj = 0; jj < GMAX; ++jj) {
+      qa[jj] = qrowA[g0 + min(jj, ng - 1)];
+      qb[jj] = qrowB[g0 + min(jj, ng - 1)];
+    }
+
+    v16i acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int jj = 0; jj < GMAX; ++jj) {
+      if (jj != 0 && jj >= ng) continue;   // ng >= 1: group 0 always runs
+      const QTables ta = make_tables(qa[jj]);
+      const QTables tb = make_tables(qb[jj]);
+      const uint32_t wa[4] = {dA[jj].x, dA[jj].y, dA[jj].z, dA[jj].w};
+      const uint32_t wb[4] = {dB[jj].x, dB[jj].y, dB[jj].z, dB[jj].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(wa[t], ta), xv[jj][t], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(wb[t], tb), xv[jj][t], acc1, 0, 0, 0);
+      }
+    }
+    // exact cross-wave reduction.  32x32 accumulator layout: lane (j, h) holds
+    // column j (token) and, in register r, row 8 (r / 4) + 4 h + (r % 4)
+    if (j < M) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+        atomicAdd(&red[row * kRedStride + j], acc0[r]);
+        atomicAdd(&red[(32 + row) * kRedStride + j], acc1[r]);
+      }
+    }
+  }
+  __syncthreads();
+
+  const int n = n0 + lane;
+  if (n >= N) return;
+  for (int t = wave; t < M; t += nw) {
+    const int s = red[lane * kRedStride + t];
+    const size_t o = static_cast<size_t>(t) * N + n;
+    if (a.slices > 1)
+      a.part[static_cast<size_t>(slice) * M * N + o] = s;
+    else if (a.out_acc)
+      static_cast<int32_t*>(a.out)[o] = s;
+    else
+      static_cast<float*>(a.out)[o] = static_cast<float>(s) * a.a_scale[t] * (a.smax[n] * (1.0f / 127.0f));
+  }
+}
+
 // Sum of the slices' partial sums in slice order, then the rescale.
 __global__ __launch_bounds__(256) void gemv_reduce_kernel(const int32_t* __restrict__ part,
                                                           int slices, int M, int N,
@@ -249,7 +352,13 @@ struct GemvPlan {
   int nw = 1;      // waves per workgroup
   int slices = 1;  // workgroups per 64-row block (K split across workgroups)
   int n_rb = 1;
+  bool mfma = false;
 };
+
+// From this many tokens on, the matrix-core kernel beats the dot4 kernel
+// (measured on both decode shapes: at 4 tokens they are about even, at 8 the
+// MFMA kernel is 1.3-1.6x faster, at 24 2.6-3.5x).
+constexpr int kMfmaMinM = 4;
 
 constexpr int kGmaxChoices[] = {2, 3, 5, 9};
 
@@ -259,21 +368,28 @@ constexpr int kGmaxChoices[] = {2, 3, 5, 9};
 constexpr double kCuBytesPerUs = 22.0e3;
 constexpr double kReduceUs = 3.5;
 
-GemvPlan make_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
+GemvPlan make_plan_for(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, bool mfma) {
   const int G = static_cast<int>(K >> 7);
   const int cus = std::max(1, dev.cu_count);
   GemvPlan best;
+  best.slices = 0;  // none found yet
   double best_t = 1e30;
-  for (int slices = 1; slices <= 8 && slices <= G; ++slices) {
+  for (int slices = 1; slices <= 32 && slices <= G; ++slices) {
     GemvPlan p;
+    p.mfma = mfma;
     p.n_rb = static_cast<int>((N + 63) / 64);
     p.slices = slices;
     const int per_slice = (G + slices - 1) / slices;
     // two or three groups per wave keeps many waves in flight; at most 16
-    // waves, at most 9 groups each
+    // waves, at most 9 groups each (MFMA kernel, for its register budget: at
+    // most 3 groups with 16 waves, 5 with 8)
     p.nw = std::min(kMaxWaves, std::max(1, per_slice / 2));
-    const int gw = (per_slice + p.nw - 1) / p.nw;
-    if (gw > 9) continue;
+    int gw = (per_slice + p.nw - 1) / p.nw;
+    if (mfma && gw > 3 && p.nw > 8) {
+      p.nw = 8;
+      gw = (per_slice + p.nw - 1) / p.nw;
+    }
+    if (gw > (mfma ? 5 : 9)) continue;
     for (int c : kGmaxChoices)
       if (c >= gw) { p.gmax = c; break; }
     const int64_t wgs = static_cast<int64_t>(p.n_rb) * slices;
@@ -284,6 +400,28 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
     if (t < best_t - 1e-9) { best_t = t; best = p; }
   }
   return best;
+}
+
+// Always returns a valid plan for 1 <= M <= 24 and K <= the library's limit:
+// the dot4 kernel takes up to 16 waves x 9 groups x 32 slices.
+GemvPlan make_plan(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceInfo& dev) {
+  const bool want_mfma = kind == kGemvMfma || (kind == kGemvAuto && M >= kMfmaMinM);
+  if (want_mfma && M <= 32) {
+    const GemvPlan p = make_plan_for(M, N, K, dev, true);
+    if (p.slices > 0) return p;
+  }
+  return make_plan_for(M, N, K, dev, false);
+}
+
+hipError_t launch_mfma(GemvArgs a, int M, const GemvPlan& pl, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(pl.n_rb * pl.slices));
+  const dim3 block(64 * pl.nw);
+  switch (pl.gmax) {
+    case 2: hipLaunchKernelGGL((gemv_mfma_kernel<2, 1024>), grid, block, 0, stream, a, M); break;
+    case 3: hipLaunchKernelGGL((gemv_mfma_kernel<3, 1024>), grid, block, 0, stream, a, M); break;
+    default: hipLaunchKernelGGL((gemv_mfma_kernel<5, 512>), grid, block, 0, stream, a, M); break;
+  }
+  return hipGetLastError();
 }
 
 template <int MT>
@@ -301,25 +439,26 @@ hipError_t launch_mt(GemvArgs a, const GemvPlan& pl, hipStream_t stream) {
 
 }  // namespace
 
-size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceInfo& dev) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  const GemvPlan pl = make_plan(M, N, K, dev);
+  const GemvPlan pl = make_plan(M, N, K, kind, dev);
   if (pl.slices <= 1) return 0;
   return static_cast<size_t>(pl.slices) * static_cast<size_t>(M) * static_cast<size_t>(N) * 4;
 }
 
 hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
                        const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
-                       void* out, bool out_acc, void* part, size_t part_bytes,
+                       void* out, bool out_acc, void* part, size_t part_bytes, GemvKind kind,
                        const DeviceInfo& dev, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  const GemvPlan pl = make_plan(M, N, K, dev);
-  if (pl.slices > 1 && (part == nullptr || part_bytes < gemv_workspace_bytes(M, N, K, dev)))
+  const GemvPlan pl = make_plan(M, N, K, kind, dev);
+  if (pl.slices <= 0 || (kind == kGemvMfma && !pl.mfma)) return hipErrorInvalidValue;
+  if (pl.slices > 1 && (part == nullptr || part_bytes < gemv_workspace_bytes(M, N, K, kind, dev)))
     return hipErrorInvalidValue;
   if (std::getenv("TWL_LOG"))
-    std::fprintf(stderr, "[twl] gemv M=%lld N=%lld K=%lld -> <= %d groups/wave, %d waves/WG, %d slices, grid=%d\n",
-                 static_cast<long long>(M), static_cast<long long>(N), static_cast<long long>(K),
-                 pl.gmax, pl.nw, pl.slices, pl.n_rb * pl.slices);
+    std::fprintf(stderr, "[twl] gemv%s M=%lld N=%lld K=%lld -> <= %d groups/wave, %d waves/WG, %d slices, grid=%d\n",
+                 pl.mfma ? "-mfma" : "", static_cast<long long>(M), static_cast<long long>(N),
+                 static_cast<long long>(K), pl.gmax, pl.nw, pl.slices, pl.n_rb * pl.slices);
   GemvArgs a;
   a.x = x_i8;
   a.a_scale = a_scale;
@@ -335,7 +474,10 @@ hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* 
   a.slices = pl.slices;
   a.out_acc = out_acc ? 1 : 0;
   hipError_t e = hipErrorInvalidValue;
-  switch (static_cast<int>(M)) {
+  if (pl.mfma) {
+    if (M > 32 || pl.nw * 64 > (pl.gmax <= 3 ? 1024 : 512)) return hipErrorInvalidValue;
+    e = launch_mfma(a, static_cast<int>(M), pl, stream);
+  } else switch (static_cast<int>(M)) {
     case 1: e = launch_mt<1>(a, pl, stream); break;
     case 2: e = launch_mt<2>(a, pl, stream); break;
     case 3: e = launch_mt<3>(a, pl, stream); break;

@@ -28,12 +28,14 @@ hipError_t launch_gemm(const int8_t* x_i8, const float* a_scale, const uint8_t* 
                        const DeviceInfo& dev, hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev);
 
-// M <= 24.  When K is split across workgroups (gemv_workspace_bytes > 0) the
-// GEMV writes int32 partial sums to `part` (at least that many bytes).
+// Decode kernels (M <= 24): kGemvAuto picks by M, kGemvDot4 / kGemvMfma force
+// one.  When K is split across workgroups (gemv_workspace_bytes > 0) the
+// kernel writes int32 partial sums to `part` (at least that many bytes).
+enum GemvKind { kGemvAuto = 0, kGemvDot4 = 1, kGemvMfma = 2 };
 hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
                        const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
-                       void* out, bool out_acc, void* part, size_t part_bytes,
+                       void* out, bool out_acc, void* part, size_t part_bytes, GemvKind kind,
                        const DeviceInfo& dev, hipStream_t stream);
-size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev);
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceInfo& dev);
 
 }  // namespace twl

@@ -72,10 +72,12 @@ def test_pack_rejects_bad_args(lib):
 
 def test_linear_rejects_bad_args(lib):
     ex = lib.twl_ternary_linear_ex
-    # unknown path
-    assert ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 1024, FAKE, 0, 7, None, 0, None) == 1
-    # GEMV path beyond its batch limit
-    assert ex(FAKE, FAKE, FAKE, FAKE, FAKE, 25, 4, 1024, FAKE, 0, 2, None, 0, None) == 2
+    # unknown paths
+    for path in (-1, 5, 7):
+        assert ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 1024, FAKE, 0, path, None, 0, None) == 1
+    # the decode paths (automatic, dot4, MFMA) beyond their batch limit
+    for path in (2, 3, 4):
+        assert ex(FAKE, FAKE, FAKE, FAKE, FAKE, 25, 4, 1024, FAKE, 0, path, None, 0, None) == 2
     # y output needs a_scale and smax; acc output does not
     assert ex(FAKE, None, FAKE, FAKE, FAKE, 4, 4, 1024, FAKE, 0, 0, None, 0, None) == 1
     assert ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 3072 + 64, FAKE, 1, 0, None, 0, None) == 2

@@ -52,7 +52,7 @@ def _check_pack(twl, code, s_bits, label):
 
 
 def _check_linear(twl, x_i8, a_scale, packed, q, smax, code, oq, osm, path, label):
-    pname = {0: "auto", 1: "gemm", 2: "gemv"}[path]
+    pname = {0: "auto", 1: "gemm", 2: "gemv", 3: "gemv-dot4", 4: "gemv-mfma"}[path]
     M, N = x_i8.shape[0], code.shape[0]
     announce(f"ternary_linear_acc {label} path={pname} M={M} N={N} K={x_i8.shape[1]}")
     acc = gpu_linear(twl, x_i8, a_scale, packed, q, smax, path, True)
@@ -101,7 +101,12 @@ def test_decode_sweep_full(twl, name):
     for M in W.DECODE_MS:
         xb = np.ascontiguousarray(layer.x_bits[:M])
         x_i8, a_scale = _check_rotq(twl, xb, layer.sign, f"{name} M={M}")
-        _check_linear(twl, x_i8, a_scale, packed, q, smax, layer.code, oq, osm, 0, f"{name} M={M}")
+        acc, _ = _check_linear(twl, x_i8, a_scale, packed, q, smax, layer.code, oq, osm, 0,
+                               f"{name} M={M}")
+        # both decode kernels, whichever the automatic choice was
+        for path in (twl.PATH_GEMV_DOT4, twl.PATH_GEMV_MFMA):
+            announce(f"ternary_linear_acc {name} M={M} path={path}")
+            assert np.array_equal(gpu_linear(twl, x_i8, a_scale, packed, q, smax, path, True), acc)
 
 
 def test_stack_sampled_layers(twl):
@@ -152,23 +157,32 @@ def test_gemm_ragged_shapes(twl, M, N, K):
     _check_linear(twl, x_i8, a_scale, packed, q, smax, layer.code, oq, osm, 1, f"ragged {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 13, 17, 24])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 13, 17, 24])
 @pytest.mark.parametrize("N,K", [(1, 1024), (65, 2048), (1000, 5120)])
 def test_gemv_vs_gemm_shapes(twl, M, N, K):
+    # every decode kernel (automatic choice, dot4, MFMA) and the GEMM against
+    # the oracle, bit-exact in acc
     layer = W.make_layer(2000 + M * 7 + N, M, K, N)
     x_i8, a_scale = O.rotate_quant_act(layer.x_bits, layer.sign)
     packed, q, smax, oq, osm = _check_pack(twl, layer.code, layer.s_bits, "gemv")
-    a1, _ = _check_linear(twl, x_i8, a_scale, packed, q, smax, layer.code, oq, osm, 2, f"gemv M={M}")
-    a2, _ = _check_linear(twl, x_i8, a_scale, packed, q, smax, layer.code, oq, osm, 1, f"gemm M={M}")
-    assert np.array_equal(a1, a2)
+    accs = []
+    for path, name in ((twl.PATH_GEMV, "gemv"), (twl.PATH_GEMV_DOT4, "dot4"),
+                       (twl.PATH_GEMV_MFMA, "decode-mfma"), (twl.PATH_GEMM, "gemm")):
+        a, _ = _check_linear(twl, x_i8, a_scale, packed, q, smax, layer.code, oq, osm, path,
+                             f"{name} M={M}")
+        accs.append(a)
+    for a in accs[1:]:
+        assert np.array_equal(accs[0], a)
 
 
+@pytest.mark.parametrize("path", ["dot4", "mfma"])
 @pytest.mark.parametrize("M,N,K", [(1, 129, 32768), (5, 64, 65536), (24, 200, 20480)])
-def test_gemv_k_split_across_workgroups(twl, M, N, K):
+def test_gemv_k_split_across_workgroups(twl, M, N, K, path):
     # K large enough that the GEMV splits it over several workgroups per row
     # block (partial sums in the workspace, added by a second kernel).
     # Repeated calls on one workspace, interleaved with a GEMM call on it,
     # must give identical results.
+    dpath = twl.PATH_GEMV_DOT4 if path == "dot4" else twl.PATH_GEMV_MFMA
     layer = W.make_layer(3000 + M + N, M, K, N, codes="sparse40")
     x_i8, a_scale = O.rotate_quant_act(layer.x_bits, layer.sign)
     packed, q, smax, oq, osm = _check_pack(twl, layer.code, layer.s_bits, "k-split")
@@ -177,10 +191,10 @@ def test_gemv_k_split_across_workgroups(twl, M, N, K):
     xi, sc = dev(x_i8), dev(a_scale)
     ws = torch.full((max(1, twl.workspace_bytes(M, N, K)),), 0x5A, dtype=torch.uint8, device="cuda")
     for rep in range(3):
-        announce(f"gemv k-split M={M} N={N} K={K} rep={rep}")
-        acc = host(twl.ternary_linear_acc(xi, packed, q, path=twl.PATH_GEMV, workspace=ws))
+        announce(f"{path} k-split M={M} N={N} K={K} rep={rep}")
+        acc = host(twl.ternary_linear_acc(xi, packed, q, path=dpath, workspace=ws))
         assert np.array_equal(acc, oacc), f"rep {rep}: acc differs"
-        y = host(twl.ternary_linear(xi, sc, packed, q, smax, path=twl.PATH_GEMV, workspace=ws))
+        y = host(twl.ternary_linear(xi, sc, packed, q, smax, path=dpath, workspace=ws))
         np.testing.assert_allclose(y, oy, rtol=Y_RTOL, atol=0)
         announce(f"gemm on the same workspace M={M} N={N} K={K} rep={rep}")
         acc2 = host(twl.ternary_linear_acc(xi, packed, q, path=twl.PATH_GEMM, workspace=ws))
