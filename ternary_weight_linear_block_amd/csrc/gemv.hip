@@ -30,9 +30,12 @@
 //   word and token, with the activations read at wave-uniform addresses
 //   through the constant address space (scalar loads, one copy per wave).
 //   Its VALU work grows with M: it is used for M < 4.
-// MFMA kernel (gemv_mfma_kernel): the tokens padded to 32 form the B operand
-//   of v_mfma_i32_32x32x32_i8 and the unpacked weights the A operand; the
-//   matrix cores make the work nearly independent of M (see the kernel).
+// MFMA kernels (4 <= M <= 24): the tokens padded to 32 form the B operand of
+//   v_mfma_i32_32x32x32_i8 and the unpacked weights the A operand, which makes
+//   the work nearly independent of M.  gemv_rows_kernel gives every CU an
+//   equal contiguous range of rows over all of K (no partial sums leave the
+//   workgroup); gemv_mfma_kernel keeps the 64-row-block split with K slices,
+//   for layers with too few rows per CU.
 #include "twl_internal.h"
 
 #include <algorithm>
@@ -325,6 +328,133 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(GemvArgs a, int M) {
   }
 }
 
+// Row-balanced matrix-core decode (M <= 32 tokens, N >= 16 rows per CU).
+// Streaming is bound per CU, so each workgroup takes an equal contiguous range
+// of rows [r0, r1) (any length up to 32 NS) over the whole of K: every CU
+// streams the same number of bytes and no partial sums leave the workgroup.
+// The rows form NS subtiles of 32 (the A operand of v_mfma_i32_32x32x32_i8;
+// rows past r1 are computed and dropped).  The waves split K into runs of at
+// most GMAX groups and keep P groups of loads in flight: group jj + P is issued
+// as soon as group jj has been consumed, so the stream and the unpack / MFMA
+// work overlap.  Loads are issued unconditionally (slots past the wave's run
+// re-read its last group) so that the compiler's vmcnt waits stay static.
+// Lane (j, h) layout as in gemv_mfma_kernel.
+template <int NS>
+struct RowGroup {
+  uint4 w[NS];   // 16 packed bytes of row 32 s + j, half h
+  v4i x[4];      // 64 activation bytes of token j, half h
+  int q[NS];
+};
+
+template <int NS, int GMAX, int P, int MAXT>
+__global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
+  static_assert(P >= 1 && P <= GMAX, "prefetch depth");
+  __shared__ int red[32 * NS * kRedStride];
+  __shared__ float row_scale[32];        // a_scale of the tokens
+  __shared__ float col_scale[32 * NS];   // smax / 127 of the rows
+  typedef int v16i __attribute__((ext_vector_type(16)));
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const int N = a.N, K = a.K, G = a.G;
+  // rows of this workgroup: an even share of N (gridDim.x shares)
+  const int r0 = static_cast<int>((static_cast<int64_t>(blockIdx.x) * N) / gridDim.x);
+  const int r1 = static_cast<int>((static_cast<int64_t>(blockIdx.x + 1) * N) / gridDim.x);
+  const int R = r1 - r0;  // 1 .. 32 NS (checked by the planner)
+
+  for (int i = threadIdx.x; i < 32 * NS * kRedStride; i += blockDim.x) red[i] = 0;
+  __syncthreads();
+
+  const int g0 = (wave * G) / nw;
+  const int ng = ((wave + 1) * G) / nw - g0;  // 0 .. GMAX
+
+  // the epilogue's scales, loaded by the last wave now and used after the
+  // main loop, so that their latency hides behind the weight stream
+  const bool scale_wave = wave == nw - 1 && !a.out_acc;
+  float sc_row = 0.0f, sc_col0 = 0.0f, sc_col1 = 0.0f;
+  if (scale_wave) {
+    if (lane < M) sc_row = a.a_scale[lane];
+    if (lane < R) sc_col0 = a.smax[r0 + lane];
+    if (lane + 64 < R) sc_col1 = a.smax[r0 + lane + 64];
+  }
+
+  if (ng > 0) {
+    const int j = lane & 31, h = lane >> 5;
+    // lanes past the last row of this workgroup re-read that row: the same
+    // cache lines, so no bytes beyond the workgroup's own rows are fetched
+    size_t wbase[NS];
+    const int8_t* qrow[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int n = min(r0 + 32 * s + j, r1 - 1);
+      wbase[s] = static_cast<size_t>(n >> 6) * G * 2048 + (n & 63) * 32 + h * 16;
+      qrow[s] = a.q + static_cast<size_t>(n) * G;
+    }
+    const int8_t* xrow = a.x + static_cast<size_t>(min(j, M - 1)) * K + h * 64;
+
+    RowGroup<NS> buf[P];
+    auto issue = [&](RowGroup<NS>& d, int jj) {
+      const int g = g0 + min(jj, ng - 1);
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        d.w[s] = *reinterpret_cast<const uint4*>(a.packed + wbase[s] + static_cast<size_t>(g) * 2048);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        d.x[t] = *reinterpret_cast<const v4i*>(xrow + static_cast<size_t>(g) * 128 + 16 * t);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) d.q[s] = qrow[s][g];
+    };
+#pragma unroll
+    for (int jj = 0; jj < P; ++jj) issue(buf[jj], jj);
+
+    v16i acc[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc[s] = v16i{0};
+#pragma unroll
+    for (int jj = 0; jj < GMAX; ++jj) {
+      RowGroup<NS>& d = buf[jj % P];
+      if (jj == 0 || jj < ng) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const QTables tab = make_tables(d.q[s]);
+          const uint32_t wv[4] = {d.w[s].x, d.w[s].y, d.w[s].z, d.w[s].w};
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            acc[s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(wv[t], tab), d.x[t], acc[s], 0, 0, 0);
+        }
+      }
+      if (jj + P < GMAX) issue(d, jj + P);
+    }
+    // exact cross-wave reduction; lane (j, h) holds token j and, in register
+    // r, row 8 (r / 4) + 4 h + (r % 4) of each subtile
+    if (j < M) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * s + 8 * (r >> 2) + 4 * h + (r & 3);
+          atomicAdd(&red[row * kRedStride + j], acc[s][r]);
+        }
+    }
+  }
+  if (scale_wave) {
+    if (lane < M) row_scale[lane] = sc_row;
+    if (lane < R) col_scale[lane] = sc_col0 * (1.0f / 127.0f);
+    if (lane + 64 < R) col_scale[lane + 64] = sc_col1 * (1.0f / 127.0f);
+  }
+  __syncthreads();
+
+  for (int i = threadIdx.x; i < M * R; i += blockDim.x) {
+    const int t = i / R, rr = i - t * R;
+    const int sum = red[rr * kRedStride + t];
+    const size_t o = static_cast<size_t>(t) * N + r0 + rr;
+    if (a.out_acc)
+      static_cast<int32_t*>(a.out)[o] = sum;
+    else
+      static_cast<float*>(a.out)[o] = static_cast<float>(sum) * row_scale[t] * col_scale[rr];
+  }
+}
+
 // Sum of the slices' partial sums in slice order, then the rescale.
 __global__ __launch_bounds__(256) void gemv_reduce_kernel(const int32_t* __restrict__ part,
                                                           int slices, int M, int N,
@@ -353,6 +483,9 @@ struct GemvPlan {
   int slices = 1;  // workgroups per 64-row block (K split across workgroups)
   int n_rb = 1;
   bool mfma = false;
+  // row-balanced MFMA kernel: `rows_wgs` workgroups of an even share of N
+  int rows_ns = 0;   // 32-row subtiles per workgroup (0: not this kernel)
+  int rows_wgs = 0;
 };
 
 // From this many tokens on, the matrix-core kernel beats the dot4 kernel
@@ -402,15 +535,75 @@ GemvPlan make_plan_for(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, b
   return best;
 }
 
+constexpr int kRowsGmaxChoices[] = {3, 5, 9, 17, 33};
+
+// Row-balanced plan: an even share of rows for every CU (a multiple of the CU
+// count of workgroups), at most 3 subtiles of 32 rows each, the whole of K
+// split over the waves.  Every workgroup reads all of x_i8 (M x K bytes) next
+// to its R x K / 4 bytes of weights, so the plan is only taken when each
+// workgroup has at least 40 rows; with fewer (the 17408 -> 5120 layer has 20
+// per CU) the K-split kernel, which shares each activation chunk among 64
+// rows, was measured faster despite its second launch.
+GemvPlan make_rows_plan(int64_t N, int64_t K, const DeviceInfo& dev) {
+  GemvPlan p;
+  p.slices = 0;
+  const int cus = std::max(1, dev.cu_count);
+  const int G = static_cast<int>(K >> 7);
+  const int64_t per_round = static_cast<int64_t>(cus) * 96;
+  const int64_t rounds = (N + per_round - 1) / per_round;
+  const int64_t wgs = rounds * cus;
+  if (N < 40 * wgs) return p;
+  const int64_t rmax = (N + wgs - 1) / wgs;
+  p.rows_ns = static_cast<int>((rmax + 31) / 32);
+  p.rows_wgs = static_cast<int>(wgs);
+  p.n_rb = static_cast<int>((N + 63) / 64);
+  p.mfma = true;
+  p.slices = 1;
+  p.nw = std::min(8, std::max(1, G));
+  const int gw = (G + p.nw - 1) / p.nw;
+  p.gmax = 0;
+  for (int c : kRowsGmaxChoices)
+    if (c >= gw) { p.gmax = c; break; }
+  if (p.gmax == 0) p.slices = 0;
+  return p;
+}
+
 // Always returns a valid plan for 1 <= M <= 24 and K <= the library's limit:
 // the dot4 kernel takes up to 16 waves x 9 groups x 32 slices.
 GemvPlan make_plan(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceInfo& dev) {
   const bool want_mfma = kind == kGemvMfma || (kind == kGemvAuto && M >= kMfmaMinM);
   if (want_mfma && M <= 32) {
+    const GemvPlan r = make_rows_plan(N, K, dev);
+    if (r.slices > 0) return r;
     const GemvPlan p = make_plan_for(M, N, K, dev, true);
     if (p.slices > 0) return p;
   }
   return make_plan_for(M, N, K, dev, false);
+}
+
+template <int NS, int MAXT>
+hipError_t launch_rows_ns(GemvArgs a, int M, const GemvPlan& pl, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(pl.rows_wgs));
+  const dim3 block(64 * pl.nw);
+  // groups of loads in flight per wave, within the register budget
+  constexpr int PM = 5;
+  switch (pl.gmax) {
+    case 3: hipLaunchKernelGGL((gemv_rows_kernel<NS, 3, 3, MAXT>), grid, block, 0, stream, a, M); break;
+    case 5: hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, PM, MAXT>), grid, block, 0, stream, a, M); break;
+    case 9: hipLaunchKernelGGL((gemv_rows_kernel<NS, 9, PM, MAXT>), grid, block, 0, stream, a, M); break;
+    case 17: hipLaunchKernelGGL((gemv_rows_kernel<NS, 17, PM, MAXT>), grid, block, 0, stream, a, M); break;
+    case 33: hipLaunchKernelGGL((gemv_rows_kernel<NS, 33, PM, MAXT>), grid, block, 0, stream, a, M); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rows(GemvArgs a, int M, const GemvPlan& pl, hipStream_t stream) {
+  switch (pl.rows_ns) {
+    case 2: return launch_rows_ns<2, 512>(a, M, pl, stream);
+    case 3: return launch_rows_ns<3, 512>(a, M, pl, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_mfma(GemvArgs a, int M, const GemvPlan& pl, hipStream_t stream) {
@@ -457,8 +650,9 @@ hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* 
     return hipErrorInvalidValue;
   if (std::getenv("TWL_LOG"))
     std::fprintf(stderr, "[twl] gemv%s M=%lld N=%lld K=%lld -> <= %d groups/wave, %d waves/WG, %d slices, grid=%d\n",
-                 pl.mfma ? "-mfma" : "", static_cast<long long>(M), static_cast<long long>(N),
-                 static_cast<long long>(K), pl.gmax, pl.nw, pl.slices, pl.n_rb * pl.slices);
+                 pl.rows_ns > 0 ? "-rows" : (pl.mfma ? "-mfma" : ""), static_cast<long long>(M),
+                 static_cast<long long>(N), static_cast<long long>(K), pl.gmax, pl.nw, pl.slices,
+                 pl.rows_ns > 0 ? pl.rows_wgs : pl.n_rb * pl.slices);
   GemvArgs a;
   a.x = x_i8;
   a.a_scale = a_scale;
@@ -474,7 +668,10 @@ hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* 
   a.slices = pl.slices;
   a.out_acc = out_acc ? 1 : 0;
   hipError_t e = hipErrorInvalidValue;
-  if (pl.mfma) {
+  if (pl.rows_ns > 0) {
+    if (M > 32 || pl.nw * 64 > 512) return hipErrorInvalidValue;
+    e = launch_rows(a, static_cast<int>(M), pl, stream);
+  } else if (pl.mfma) {
     if (M > 32 || pl.nw * 64 > (pl.gmax <= 3 ? 1024 : 512)) return hipErrorInvalidValue;
     e = launch_mfma(a, static_cast<int>(M), pl, stream);
   } else switch (static_cast<int>(M)) {
