@@ -104,14 +104,15 @@ def graph_time_ms(torch, fn, iters: int, replays: int = 3) -> float:
     return best
 
 
-def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, kernel_iters=50):
+def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, kernel_iters=50, bf16=False):
     """warmup + timed steps of rotate_quant_act + ternary_linear.
 
     Returns (ms per step from the wall clock around exactly `steps` eager
     steps, mean ms of one rotate_quant_act launch, mean ms of one
     ternary_linear call); the per-kernel means come from HIP events around a
     captured graph of `kernel_iters` back-to-back launches of that kernel alone
-    (weights cycled), see graph_time_ms.
+    (weights cycled), see graph_time_ms.  With bf16=True a fourth value is
+    the mean ms of one ternary_linear call that writes y in bf16 instead.
     """
     M, K = x.shape
     N = sets[0][2].shape[0]
@@ -147,7 +148,17 @@ def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, kernel_iters=50):
         ctr[0] += 1
 
     lin = graph_time_ms(torch, linear_next, kernel_iters)
-    return ms_step, rq, lin
+    if not bf16:
+        return ms_step, rq, lin
+    y16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def linear_bf16_next():
+        packed, q, smax = sets[ctr[0] % len(sets)]
+        twl.ternary_linear_bf16(x_i8, a_scale, packed, q, smax, out=y16, workspace=ws)
+        ctr[0] += 1
+
+    lin16 = graph_time_ms(torch, linear_bf16_next, kernel_iters)
+    return ms_step, rq, lin, lin16
 
 
 def traffic_for(kernel_src: str, workload: str):
@@ -210,11 +221,13 @@ def section_layer(torch, twl, name, steps, warmup):
     import workloads as W
     layer = W.make_config(name)
     x, sign, sets = upload_layer(torch, twl, layer, n_copies(layer.N, layer.K))
-    ms, rq, lin = run_layer_steps(torch, twl, x, sign, sets, steps, warmup)
+    ms, rq, lin, lin16 = run_layer_steps(torch, twl, x, sign, sets, steps, warmup, bf16=True)
     ops = 2.0 * layer.M * layer.N * layer.K
     out = {"M": layer.M, "K": layer.K, "N": layer.N, "ms_per_step": round(ms, 5),
            "step_tops": round(ops / ms / 1e9, 2), "linear_ms": round(lin, 5),
-           "linear_tops": round(ops / lin / 1e9, 2), "rotq_ms": round(rq, 5),
+           "linear_tops": round(ops / lin / 1e9, 2),
+           "linear_bf16_y_ms": round(lin16, 5), "linear_bf16_y_tops": round(ops / lin16 / 1e9, 2),
+           "rotq_ms": round(rq, 5),
            "rotq_gbs": round((layer.M * layer.K * 3 + layer.M * 4 + layer.K) / rq / 1e6, 1),
            "weight_copies": len(sets)}
     del sets, x

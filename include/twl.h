@@ -145,16 +145,26 @@ twl_status twl_ternary_linear_acc(const int8_t* x_i8, const uint8_t* packed, con
                                   int64_t M, int64_t N, int64_t K, int32_t* acc,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* What twl_ternary_linear_ex writes into `out` [M, N]. */
+typedef enum {
+  TWL_OUT_F32 = 0,      /* y, fp32                                              */
+  TWL_OUT_ACC_I32 = 1,  /* the exact int32 accumulators (no rescale)            */
+  TWL_OUT_BF16 = 2      /* y rounded to bf16 (nearest even), as uint16 bit patterns;
+                           the same fp32 value as TWL_OUT_F32 before rounding   */
+} twl_out;
+
 /*
- * ternary_linear_ex -- explicit kernel family.  out_acc != 0 writes int32 acc
- * into `out` (a_scale and smax are then ignored and may be NULL), otherwise fp32
- * y.  The decode paths (TWL_PATH_GEMV, _GEMV_DOT4, _GEMV_MFMA) require
+ * ternary_linear_ex -- explicit output kind and kernel family.  out_kind is a
+ * twl_out: with TWL_OUT_ACC_I32, a_scale and smax are ignored and may be NULL.
+ * The bf16 output halves the bytes of y, which dominate the prefill step's
+ * traffic (the pages' consumers take bf16 activations, [P1] section 4).
+ * The decode paths (TWL_PATH_GEMV, _GEMV_DOT4, _GEMV_MFMA) require
  * M <= TWL_GEMV_MAX_M; TWL_PATH_GEMV picks the dot4 kernel for the smallest
  * batches and the MFMA kernel above.  All paths give bit-identical acc.
  */
 twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
                                  const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
-                                 void* out, int out_acc, int path,
+                                 void* out, int out_kind, int path,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */

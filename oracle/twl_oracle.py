@@ -40,7 +40,9 @@ Readings taken where the pages are silent (each is listed in the design notes):
   tile (r, g) at byte (r * K/128 + g) * 2048, row 64r + j at 32 j inside it,
   rows past N padded with code 0;  R11 the
   epilogue y = acc * a_scale[t] * smax[n] / 127 is evaluated in float64 and
-  rounded to fp32 once.
+  rounded to fp32 once;  R12 the optional bf16 output is that fp32 y rounded
+  to the nearest bf16 value, ties to even (the pages' consumers take bf16
+  activations, [P1] section 4; they do not say how y is narrowed).
 """
 from __future__ import annotations
 
@@ -281,6 +283,25 @@ def epilogue_at(acc_s: np.ndarray, a_scale: np.ndarray, smax: np.ndarray, rows, 
 def ternary_linear(x_i8, a_scale, code, q, smax):
     """Full prefill/decode linear: int32 acc then the per-token/per-row rescale."""
     return epilogue(linear_acc(x_i8, code, q), a_scale, smax)
+
+
+def round_bf16(y: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), nearest value, ties to even (R12).
+
+    Written from the definition: the two bf16 neighbours of y (its fp32 bits
+    truncated to the top 16, and the next bf16 value away from zero) are
+    compared in float64, and on a tie the one with an even last bit wins.
+    Finite inputs only."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    u = y.view(np.uint32)
+    lo_bits = u & np.uint32(0xFFFF0000)
+    hi_bits = lo_bits + np.uint32(0x10000)
+    y64 = y.astype(np.float64)
+    d_lo = np.abs(y64 - lo_bits.view(np.float32).astype(np.float64))
+    d_hi = np.abs(hi_bits.view(np.float32).astype(np.float64) - y64)
+    lo_odd = ((lo_bits >> 16) & 1) == 1
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & lo_odd)
+    return np.where(take_hi, hi_bits >> 16, lo_bits >> 16).astype(np.uint16)
 
 
 # ---------------------------------------------------------------------------

@@ -20,7 +20,7 @@ from ._lib import (GEMV_MAX_M, GROUP, HBLOCK, MAX_K, PATH_AUTO, PATH_GEMM, PATH_
                    PATH_GEMV_MFMA, TwlError)
 
 __all__ = [
-    "rotate_quant_act", "pack_ternary", "ternary_linear", "ternary_linear_acc",
+    "rotate_quant_act", "pack_ternary", "ternary_linear", "ternary_linear_acc", "ternary_linear_bf16",
     "workspace_bytes", "packed_bytes", "TwlError", "PATH_AUTO", "PATH_GEMM", "PATH_GEMV", "PATH_GEMV_DOT4",
     "PATH_GEMV_MFMA", "GEMV_MAX_M",
     "HBLOCK", "GROUP", "MAX_K", "library",
@@ -101,7 +101,7 @@ def workspace_bytes(M: int, N: int, K: int) -> int:
     return int(_lib.load().twl_workspace_bytes(M, N, K))
 
 
-def _linear(x_i8, a_scale, packed, q, smax, out_acc: bool, path: int, out=None, workspace=None,
+def _linear(x_i8, a_scale, packed, q, smax, out_kind: int, path: int, out=None, workspace=None,
             stream=None):
     torch = _torch()
     lib = _lib.load()
@@ -111,8 +111,11 @@ def _linear(x_i8, a_scale, packed, q, smax, out_acc: bool, path: int, out=None, 
         raise ValueError(f"q has shape {tuple(q.shape)}, expected [N, K/128] with K = {K}")
     if N > 0 and packed.numel() != packed_bytes(N, K):
         raise ValueError(f"packed has {packed.numel()} bytes, expected {packed_bytes(N, K)}")
+    out_acc = out_kind == _lib.OUT_ACC_I32
+    out_dtype = {_lib.OUT_F32: torch.float32, _lib.OUT_ACC_I32: torch.int32,
+                 _lib.OUT_BF16: torch.bfloat16}[out_kind]
     if out is None:
-        out = torch.empty((M, N), dtype=torch.int32 if out_acc else torch.float32, device=x_i8.device)
+        out = torch.empty((M, N), dtype=out_dtype, device=x_i8.device)
     need = workspace_bytes(M, N, K)
     ws_ptr, ws_len = None, 0
     if need:
@@ -124,8 +127,8 @@ def _linear(x_i8, a_scale, packed, q, smax, out_acc: bool, path: int, out=None, 
         None if out_acc else _dev_ptr(a_scale, "a_scale", (torch.float32,)),
         _dev_ptr(packed, "packed", (torch.uint8,)), _dev_ptr(q, "q", (torch.int8,)),
         None if out_acc else _dev_ptr(smax, "smax", (torch.float32,)),
-        M, N, K, _dev_ptr(out, "out", (torch.int32,) if out_acc else (torch.float32,)),
-        1 if out_acc else 0, path, ws_ptr, ws_len, _stream_handle(stream))
+        M, N, K, _dev_ptr(out, "out", (out_dtype,)),
+        out_kind, path, ws_ptr, ws_len, _stream_handle(stream))
     _lib.check(st, "twl_ternary_linear_ex")
     return out
 
@@ -133,10 +136,16 @@ def _linear(x_i8, a_scale, packed, q, smax, out_acc: bool, path: int, out=None, 
 def ternary_linear(x_i8, a_scale, packed, q, smax, path: int = PATH_AUTO, out=None,
                    workspace=None, stream=None):
     """y [M, N] fp32 = (sum_k x_i8 * code * q) * a_scale[t] * smax[n] / 127."""
-    return _linear(x_i8, a_scale, packed, q, smax, False, path, out, workspace, stream)
+    return _linear(x_i8, a_scale, packed, q, smax, _lib.OUT_F32, path, out, workspace, stream)
+
+
+def ternary_linear_bf16(x_i8, a_scale, packed, q, smax, path: int = PATH_AUTO, out=None,
+                        workspace=None, stream=None):
+    """The same y rounded to bf16 (nearest even) in the kernels' epilogue."""
+    return _linear(x_i8, a_scale, packed, q, smax, _lib.OUT_BF16, path, out, workspace, stream)
 
 
 def ternary_linear_acc(x_i8, packed, q, path: int = PATH_AUTO, out=None, workspace=None,
                        stream=None):
     """The exact int32 accumulators acc [M, N] of the same kernels (no rescale)."""
-    return _linear(x_i8, None, packed, q, None, True, path, out, workspace, stream)
+    return _linear(x_i8, None, packed, q, None, _lib.OUT_ACC_I32, path, out, workspace, stream)

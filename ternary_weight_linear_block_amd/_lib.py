@@ -15,6 +15,7 @@ TWL_OK = 0
 STATUS_NAMES = {0: "TWL_OK", 1: "TWL_EINVAL", 2: "TWL_ESHAPE", 3: "TWL_EALIGN",
                 4: "TWL_EDEVICE", 5: "TWL_EHIP"}
 PATH_AUTO, PATH_GEMM, PATH_GEMV, PATH_GEMV_DOT4, PATH_GEMV_MFMA = 0, 1, 2, 3, 4
+OUT_F32, OUT_ACC_I32, OUT_BF16 = 0, 1, 2
 HBLOCK, GROUP, MAX_K, GEMV_MAX_M = 1024, 128, 65536, 24
 
 # (name, restype, argtypes) for every symbol include/twl.h declares

@@ -101,7 +101,7 @@ extern "C" {
 
 const char* twl_last_error(void) { return g_last_error.c_str(); }
 
-int twl_abi_version(void) { return 2; }
+int twl_abi_version(void) { return 3; }
 
 size_t twl_packed_bytes(int64_t N, int64_t K) {
   if (N <= 0 || K <= 0 || K % TWL_HBLOCK != 0 || K > TWL_MAX_K || N > (int64_t{1} << 30)) return 0;
@@ -157,13 +157,15 @@ size_t twl_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 
 twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
                                  const int8_t* q, const float* smax, int64_t M, int64_t N,
-                                 int64_t K, void* out, int out_acc, int path, void* workspace,
+                                 int64_t K, void* out, int out_kind, int path, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
   TWL_TRY(check_rows("M", M));
   TWL_TRY(check_rows("N", N));
   TWL_TRY(check_k(K));
   if (path < TWL_PATH_AUTO || path > TWL_PATH_GEMV_MFMA)
     return fail(TWL_EINVAL, "unknown path %d", path);
+  if (out_kind < TWL_OUT_F32 || out_kind > TWL_OUT_BF16)
+    return fail(TWL_EINVAL, "unknown output kind %d", out_kind);
   const bool decode_path = path >= TWL_PATH_GEMV;
   if (decode_path && M > TWL_GEMV_MAX_M)
     return fail(TWL_ESHAPE, "the decode paths take M <= %d (got %lld)", TWL_GEMV_MAX_M,
@@ -173,7 +175,7 @@ twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const
   TWL_REQUIRE_PTR(packed);
   TWL_REQUIRE_PTR(q);
   TWL_REQUIRE_PTR(out);
-  if (!out_acc) {
+  if (out_kind != TWL_OUT_ACC_I32) {
     TWL_REQUIRE_PTR(a_scale);
     TWL_REQUIRE_PTR(smax);
   }
@@ -192,11 +194,13 @@ twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const
     if (!aligned16(workspace)) return fail(TWL_EALIGN, "workspace is not 16-byte aligned");
   }
   if (use_gemv)
-    return launched(twl::launch_gemv(x_i8, a_scale, packed, q, smax, M, N, K, out, out_acc != 0,
-                                     workspace, workspace_bytes, kind, dev, stream),
+    return launched(twl::launch_gemv(x_i8, a_scale, packed, q, smax, M, N, K, out,
+                                     static_cast<twl::OutKind>(out_kind), workspace,
+                                     workspace_bytes, kind, dev, stream),
                     "ternary_linear (GEMV)");
-  return launched(twl::launch_gemm(x_i8, a_scale, packed, q, smax, M, N, K, out, out_acc != 0,
-                                   workspace, workspace_bytes, dev, stream),
+  return launched(twl::launch_gemm(x_i8, a_scale, packed, q, smax, M, N, K, out,
+                                   static_cast<twl::OutKind>(out_kind), workspace,
+                                   workspace_bytes, dev, stream),
                   "ternary_linear (GEMM)");
 }
 
@@ -204,14 +208,14 @@ twl_status twl_ternary_linear(const int8_t* x_i8, const float* a_scale, const ui
                               const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
                               float* y, void* workspace, size_t workspace_bytes,
                               hipStream_t stream) {
-  return twl_ternary_linear_ex(x_i8, a_scale, packed, q, smax, M, N, K, y, 0, TWL_PATH_AUTO,
+  return twl_ternary_linear_ex(x_i8, a_scale, packed, q, smax, M, N, K, y, TWL_OUT_F32, TWL_PATH_AUTO,
                                workspace, workspace_bytes, stream);
 }
 
 twl_status twl_ternary_linear_acc(const int8_t* x_i8, const uint8_t* packed, const int8_t* q,
                                   int64_t M, int64_t N, int64_t K, int32_t* acc, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
-  return twl_ternary_linear_ex(x_i8, nullptr, packed, q, nullptr, M, N, K, acc, 1, TWL_PATH_AUTO,
+  return twl_ternary_linear_ex(x_i8, nullptr, packed, q, nullptr, M, N, K, acc, TWL_OUT_ACC_I32, TWL_PATH_AUTO,
                                workspace, workspace_bytes, stream);
 }
 

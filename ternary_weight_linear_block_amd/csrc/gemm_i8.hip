@@ -193,33 +193,108 @@ struct GemmArgs {
 // per-row / per-column scales (staged in LDS) or the raw int32 accumulators.
 // 32x32 accumulator layout: lane holds column l32 of a fragment; register r
 // holds row 8 (r / 4) + 4 half + (r % 4).
-template <int RM, int FN, bool OUT_ACC>
+// Writes one wave's RM x RN fragments of the output tile: fp32 or bf16 y with
+// the per-row / per-column scales (staged in LDS), or the raw int32
+// accumulators.  32x32 accumulator layout: lane holds column l32 of a
+// fragment; register r holds row 8 (r / 4) + 4 half + (r % 4).  Stored as is,
+// every store instruction would cover only two 128-byte row pieces, and the
+// output phase is bound by the number of store transactions (halving the
+// bytes with bf16 was measured not to shorten it).  So when N % 4 == 0 each
+// fragment goes through this wave's LDS scratch `tr` (32 rows x kTrStride
+// words; the stride puts the two lane halves' writes on different banks) and
+// comes back as 4 consecutive columns per lane: one 16-byte (8 for bf16)
+// store per lane covers 8 rows of the fragment.
+constexpr int kTrStride = 40;
+
+// two fp32 values (as bit patterns) -> two bf16 in one dword, low one first
+__device__ __forceinline__ uint32_t bf16_pair(int lo_bits, int hi_bits) {
+  return f32_to_bf16_rne(__int_as_float(lo_bits)) |
+         (static_cast<uint32_t>(f32_to_bf16_rne(__int_as_float(hi_bits))) << 16);
+}
+
+__device__ __forceinline__ void lds_wave_sync() {
+  // LDS operations of one wave execute in order; the fences only keep the
+  // compiler from moving the reads of other lanes' data above the writes (or
+  // the next writes above these reads)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int RM, int FN, int OUT>
 __device__ __forceinline__ void store_tile(const v16i (&acc)[RM][(FN + 1) / 2], void* out,
                                            const float* row_scale, const float* col_scale,
                                            int M, int N, int m0, int n0, int wm, int wn,
-                                           int lane) {
+                                           int lane, int32_t* tr) {
   constexpr int RN = (FN + 1) / 2;
   const int l32 = lane & 31, half = lane >> 5;
+  const bool vec = (N & 3) == 0;
 #pragma unroll
   for (int j = 0; j < RN; ++j) {
     const int f = wn * RN + j;
     if (f >= FN) continue;  // padding fragment
     const int cl = 32 * f + l32;
     const int col = n0 + cl;
-    if (col >= N) continue;
-    const float cscale = OUT_ACC ? 0.0f : col_scale[cl] * (1.0f / 127.0f);
+    if (!vec && col >= N) continue;
+    const float cscale = OUT == kOutAcc ? 0.0f : col_scale[cl] * (1.0f / 127.0f);
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
+      const int rbase = wm * 32 * RM + 32 * i;  // first row of the fragment in the tile
+      if (!vec) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = rbase + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int row = m0 + rl;
+          if (row < M) {
+            const size_t o = static_cast<size_t>(row) * N + col;
+            const float v = OUT == kOutAcc ? 0.0f : static_cast<float>(acc[i][j][r]) * row_scale[rl] * cscale;
+            store_out(out, o, OUT, acc[i][j][r], v);
+          }
+        }
+        continue;
+      }
+      lds_wave_sync();  // the previous fragment's reads are done
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int rl = wm * 32 * RM + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-        const int row = m0 + rl;
-        if (row < M) {
-          const size_t o = static_cast<size_t>(row) * N + col;
-          if (OUT_ACC)
-            static_cast<int32_t*>(out)[o] = acc[i][j][r];
+        const int rr = 8 * (r >> 2) + 4 * half + (r & 3);
+        const int bits = OUT == kOutAcc
+                             ? acc[i][j][r]
+                             : __float_as_int(static_cast<float>(acc[i][j][r]) * row_scale[rbase + rr] * cscale);
+        tr[rr * kTrStride + l32] = bits;
+      }
+      lds_wave_sync();
+      if (OUT == kOutBf16 && (N & 7) == 0) {
+        // 8 columns per lane: one 16-byte store covers 16 rows of the fragment
+        const int c8 = 8 * (lane & 3);
+        const int gcol = n0 + 32 * f + c8;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int rr = 16 * k + (lane >> 2);
+          const v4i a = *reinterpret_cast<const v4i*>(tr + rr * kTrStride + c8);
+          const v4i b = *reinterpret_cast<const v4i*>(tr + rr * kTrStride + c8 + 4);
+          const int grow = m0 + rbase + rr;
+          if (grow < M && gcol < N) {  // N % 8 == 0: all eight columns are in range
+            const uint4 w = make_uint4(bf16_pair(a.x, a.y), bf16_pair(a.z, a.w), bf16_pair(b.x, b.y),
+                                       bf16_pair(b.z, b.w));
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + static_cast<size_t>(grow) * N + gcol) = w;
+          }
+        }
+        continue;
+      }
+      const int c4 = 4 * (lane & 7);
+      const int gcol = n0 + 32 * f + c4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int rr = 8 * k + (lane >> 3);
+        const v4i v = *reinterpret_cast<const v4i*>(tr + rr * kTrStride + c4);
+        const int grow = m0 + rbase + rr;
+        if (grow < M && gcol < N) {  // N % 4 == 0: all four columns are in range
+          const size_t o = static_cast<size_t>(grow) * N + gcol;
+          if (OUT == kOutBf16)
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) =
+                make_uint2(bf16_pair(v.x, v.y), bf16_pair(v.z, v.w));
           else
-            static_cast<float*>(out)[o] = static_cast<float>(acc[i][j][r]) * row_scale[rl] * cscale;
+            *reinterpret_cast<v4i*>(static_cast<int32_t*>(out) + o) = v;
         }
       }
     }
@@ -247,7 +322,7 @@ __device__ __forceinline__ WorkItem work_item(int bid, int tiles_m, int tiles_n,
   return w;
 }
 
-template <int RM, int FN, int WK, bool OUT_ACC>
+template <int RM, int FN, int WK, int OUT>
 __global__ __launch_bounds__(64 * 4 * WK, 1) void gemm_kernel(GemmArgs p) {
   using T = Tile<RM, FN, WK>;
   constexpr int RN = T::RN, BN = T::BN;
@@ -258,6 +333,8 @@ __global__ __launch_bounds__(64 * 4 * WK, 1) void gemm_kernel(GemmArgs p) {
   // output stores would order every load behind the stores before it)
   __shared__ __attribute__((aligned(16))) float row_scale[T::BM];
   __shared__ __attribute__((aligned(16))) float col_scale[(T::BN + 63) / 64 * 64];
+  // output transposes of the four storing waves
+  __shared__ __attribute__((aligned(16))) int32_t tr_lds[4][32 * kTrStride];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -295,7 +372,7 @@ __global__ __launch_bounds__(64 * 4 * WK, 1) void gemm_kernel(GemmArgs p) {
       dma4(sgpr_ptr(q_tile), static_cast<uint32_t>((min(n0 + c, N - 1) - n0) * G + g0 + 4 * d),
            __builtin_amdgcn_readfirstlane(q_base + ii * 256));
     }
-    if (!OUT_ACC) {
+    if (OUT != kOutAcc) {
       const uint32_t r_base = lds_addr(row_scale), c_base = lds_addr(col_scale);
       for (int ii = wave; ii < T::BM / 64; ii += T::NW)
         dma4(sgpr_ptr(p.a_scale + m0), static_cast<uint32_t>((min(m0 + ii * 64 + lane, M - 1) - m0) * 4),
@@ -519,23 +596,25 @@ __global__ __launch_bounds__(64 * 4 * WK, 1) void gemm_kernel(GemmArgs p) {
         }
     return;
   }
-  store_tile<RM, FN, OUT_ACC>(acc, p.out, row_scale, col_scale, M, N, m0, n0, wm, wn, lane);
+  store_tile<RM, FN, OUT>(acc, p.out, row_scale, col_scale, M, N, m0, n0, wm, wn, lane,
+                          tr_lds[wave & 3]);
 }
 
 // Split-K second pass: one workgroup per block tile, four waves in the same
 // (wm, wn) roles as the GEMM's wk = 0 waves; adds the splits' partial tiles
 // (exact int32) and runs the same epilogue.
-template <int RM, int FN, bool OUT_ACC>
+template <int RM, int FN, int OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
   using T = Tile<RM, FN, 1>;
   constexpr int RN = T::RN;
   __shared__ float row_scale[T::BM];
   __shared__ float col_scale[T::BN];
+  __shared__ __attribute__((aligned(16))) int32_t tr_lds[4][32 * kTrStride];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tile = blockIdx.x;
   const int m0 = (tile % p.tiles_m) * T::BM, n0 = (tile / p.tiles_m) * T::BN;
-  if (!OUT_ACC) {
+  if (OUT != kOutAcc) {
     for (int r = tid; r < T::BM; r += 256) row_scale[r] = p.a_scale[min(m0 + r, p.M - 1)];
     for (int c = tid; c < T::BN; c += 256) col_scale[c] = p.smax[min(n0 + c, p.N - 1)];
   }
@@ -561,8 +640,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
         }
   }
   __syncthreads();
-  store_tile<RM, FN, OUT_ACC>(acc, p.out, row_scale, col_scale, p.M, p.N, m0, n0, wave & 1,
-                              wave >> 1, lane);
+  store_tile<RM, FN, OUT>(acc, p.out, row_scale, col_scale, p.M, p.N, m0, n0, wave & 1,
+                          wave >> 1, lane, tr_lds[wave]);
 }
 
 // ---------------------------------------------------------------- planner
@@ -648,22 +727,25 @@ size_t plan_workspace_bytes(const Plan& pl) {
   return tiles * pl.splits * pl.slot_ints * sizeof(int32_t);
 }
 
-template <int RM, int FN, int WK>
-hipError_t launch_cfg(const GemmArgs& a, bool out_acc, hipStream_t stream) {
+template <int RM, int FN, int WK, int OUT>
+hipError_t launch_cfg_out(const GemmArgs& a, hipStream_t stream) {
   using T = Tile<RM, FN, WK>;
   const unsigned tiles = static_cast<unsigned>(a.tiles_m) * a.tiles_n;
   const unsigned grid = tiles * a.splits;
-  if (out_acc)
-    hipLaunchKernelGGL((gemm_kernel<RM, FN, WK, true>), dim3(grid), dim3(T::THREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL((gemm_kernel<RM, FN, WK, false>), dim3(grid), dim3(T::THREADS), 0, stream, a);
+  hipLaunchKernelGGL((gemm_kernel<RM, FN, WK, OUT>), dim3(grid), dim3(T::THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits <= 1) return e;
-  if (out_acc)
-    hipLaunchKernelGGL((splitk_reduce_kernel<RM, FN, true>), dim3(tiles), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((splitk_reduce_kernel<RM, FN, false>), dim3(tiles), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((splitk_reduce_kernel<RM, FN, OUT>), dim3(tiles), dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int RM, int FN, int WK>
+hipError_t launch_cfg(const GemmArgs& a, OutKind out_kind, hipStream_t stream) {
+  switch (out_kind) {
+    case kOutAcc: return launch_cfg_out<RM, FN, WK, kOutAcc>(a, stream);
+    case kOutBf16: return launch_cfg_out<RM, FN, WK, kOutBf16>(a, stream);
+    default: return launch_cfg_out<RM, FN, WK, kOutF32>(a, stream);
+  }
 }
 
 }  // namespace
@@ -675,7 +757,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const DeviceInfo& d
 
 hipError_t launch_gemm(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
                        const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
-                       void* out, bool out_acc, void* workspace, size_t, const DeviceInfo& dev,
+                       void* out, OutKind out_kind, void* workspace, size_t, const DeviceInfo& dev,
                        hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const Plan pl = make_plan(M, N, K, std::max(1, dev.cu_count));
@@ -702,7 +784,7 @@ hipError_t launch_gemm(const int8_t* x_i8, const float* a_scale, const uint8_t* 
   a.splits = pl.splits;
   a.stages_per_split = pl.stages_per_split;
 #define TWL_CFG(RM_, FN_, WK_) \
-  if (pl.rm == RM_ && pl.fn == FN_ && pl.wk == WK_) return launch_cfg<RM_, FN_, WK_>(a, out_acc, stream);
+  if (pl.rm == RM_ && pl.fn == FN_ && pl.wk == WK_) return launch_cfg<RM_, FN_, WK_>(a, out_kind, stream);
   TWL_CFG(1, 4, 2)
   TWL_CFG(1, 8, 2)
   TWL_CFG(1, 10, 2)

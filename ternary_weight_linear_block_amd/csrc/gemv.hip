@@ -87,12 +87,12 @@ struct GemvArgs {
   const uint8_t* packed;
   const int8_t* q;
   const float* smax;
-  void* out;          // float y [M,N] or int32 acc [M,N]
+  void* out;          // y [M,N] (fp32 or bf16) or int32 acc [M,N]
   int32_t* part;      // [slices][M][N] int32 partial sums when slices > 1
   int N, K, G;        // G = K / 128
   int n_rb;           // 64-row blocks
   int slices;         // workgroups per row block (K split across workgroups)
-  int out_acc;
+  int out_kind;       // OutKind
 };
 
 // v_permlane32_swap_b32 exchanges lanes 32..63 of its first operand with lanes
@@ -205,11 +205,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a) {
   const int n = n0 + lane;
   auto finish = [&](int t, int s) {
     const size_t o = static_cast<size_t>(t) * N + n;
-    if (a.out_acc)
-      static_cast<int32_t*>(a.out)[o] = s;
-    else
-      static_cast<float*>(a.out)[o] =
-          static_cast<float>(s) * a.a_scale[t] * (a.smax[n] * (1.0f / 127.0f));
+    const float v = a.out_kind == kOutAcc
+                        ? 0.0f
+                        : static_cast<float>(s) * a.a_scale[t] * (a.smax[n] * (1.0f / 127.0f));
+    store_out(a.out, o, a.out_kind, s, v);
   };
   if (a.slices == 1) {
     if (n < N)
@@ -321,10 +320,10 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(GemvArgs a, int M) {
     const size_t o = static_cast<size_t>(t) * N + n;
     if (a.slices > 1)
       a.part[static_cast<size_t>(slice) * M * N + o] = s;
-    else if (a.out_acc)
-      static_cast<int32_t*>(a.out)[o] = s;
     else
-      static_cast<float*>(a.out)[o] = static_cast<float>(s) * a.a_scale[t] * (a.smax[n] * (1.0f / 127.0f));
+      store_out(a.out, o, a.out_kind, s,
+                a.out_kind == kOutAcc ? 0.0f
+                                      : static_cast<float>(s) * a.a_scale[t] * (a.smax[n] * (1.0f / 127.0f)));
   }
 }
 
@@ -370,7 +369,7 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
 
   // the epilogue's scales, loaded by the last wave now and used after the
   // main loop, so that their latency hides behind the weight stream
-  const bool scale_wave = wave == nw - 1 && !a.out_acc;
+  const bool scale_wave = wave == nw - 1 && a.out_kind != kOutAcc;
   float sc_row = 0.0f, sc_col0 = 0.0f, sc_col1 = 0.0f;
   if (scale_wave) {
     if (lane < M) sc_row = a.a_scale[lane];
@@ -448,10 +447,8 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
     const int t = i / R, rr = i - t * R;
     const int sum = red[rr * kRedStride + t];
     const size_t o = static_cast<size_t>(t) * N + r0 + rr;
-    if (a.out_acc)
-      static_cast<int32_t*>(a.out)[o] = sum;
-    else
-      static_cast<float*>(a.out)[o] = static_cast<float>(sum) * row_scale[t] * col_scale[rr];
+    store_out(a.out, o, a.out_kind, sum,
+              a.out_kind == kOutAcc ? 0.0f : static_cast<float>(sum) * row_scale[t] * col_scale[rr]);
   }
 }
 
@@ -460,20 +457,20 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const int32_t* __restr
                                                           int slices, int M, int N,
                                                           const float* __restrict__ a_scale,
                                                           const float* __restrict__ smax,
-                                                          void* __restrict__ out, int out_acc) {
+                                                          void* __restrict__ out, int out_kind) {
   const size_t total = static_cast<size_t>(M) * N;
   const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
   for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
        i += stride) {
     int s = 0;
     for (int sl = 0; sl < slices; ++sl) s += part[static_cast<size_t>(sl) * total + i];
-    if (out_acc) {
-      static_cast<int32_t*>(out)[i] = s;
-    } else {
+    float v = 0.0f;
+    if (out_kind != kOutAcc) {
       const int t = static_cast<int>(i / static_cast<size_t>(N));
       const int n = static_cast<int>(i - static_cast<size_t>(t) * N);
-      static_cast<float*>(out)[i] = static_cast<float>(s) * a_scale[t] * (smax[n] * (1.0f / 127.0f));
+      v = static_cast<float>(s) * a_scale[t] * (smax[n] * (1.0f / 127.0f));
     }
+    store_out(out, i, out_kind, s, v);
   }
 }
 
@@ -641,7 +638,7 @@ size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, GemvKind kind, cons
 
 hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
                        const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
-                       void* out, bool out_acc, void* part, size_t part_bytes, GemvKind kind,
+                       void* out, OutKind out_kind, void* part, size_t part_bytes, GemvKind kind,
                        const DeviceInfo& dev, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const GemvPlan pl = make_plan(M, N, K, kind, dev);
@@ -666,7 +663,7 @@ hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* 
   a.G = static_cast<int>(K >> 7);
   a.n_rb = pl.n_rb;
   a.slices = pl.slices;
-  a.out_acc = out_acc ? 1 : 0;
+  a.out_kind = out_kind;
   hipError_t e = hipErrorInvalidValue;
   if (pl.rows_ns > 0) {
     if (M > 32 || pl.nw * 64 > 512) return hipErrorInvalidValue;
@@ -705,7 +702,7 @@ hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* 
   const size_t total = static_cast<size_t>(M) * static_cast<size_t>(N);
   const unsigned blocks = static_cast<unsigned>(std::min<size_t>((total + 255) / 256, 4096));
   hipLaunchKernelGGL(gemv_reduce_kernel, dim3(blocks), dim3(256), 0, stream, a.part, pl.slices,
-                     static_cast<int>(M), a.N, a_scale, smax, out, a.out_acc);
+                     static_cast<int>(M), a.N, a_scale, smax, out, a.out_kind);
   return hipGetLastError();
 }
 

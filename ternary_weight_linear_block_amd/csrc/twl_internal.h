@@ -21,10 +21,30 @@ hipError_t launch_pack(const int8_t* code, const uint16_t* s, int64_t N, int64_t
                        uint8_t* packed, int8_t* q, float* smax, int32_t* bad_codes,
                        hipStream_t stream);
 
-// out is float* (y) when out_acc is false, int32_t* (acc) otherwise.
+// What the linear layer writes: fp32 y, the raw int32 accumulators, or y
+// rounded to bf16 (round to nearest even).
+enum OutKind { kOutF32 = 0, kOutAcc = 1, kOutBf16 = 2 };
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Stores one epilogue value v (y before rounding) or the accumulator s at
+// element o of `out`, whose type follows `kind`.
+__device__ __forceinline__ void store_out(void* out, size_t o, int kind, int32_t s, float v) {
+  if (kind == kOutAcc)
+    static_cast<int32_t*>(out)[o] = s;
+  else if (kind == kOutBf16)
+    static_cast<uint16_t*>(out)[o] = f32_to_bf16_rne(v);
+  else
+    static_cast<float*>(out)[o] = v;
+}
+
 hipError_t launch_gemm(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
                        const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
-                       void* out, bool out_acc, void* workspace, size_t workspace_bytes,
+                       void* out, OutKind out_kind, void* workspace, size_t workspace_bytes,
                        const DeviceInfo& dev, hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev);
 
@@ -34,7 +54,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const DeviceInfo& d
 enum GemvKind { kGemvAuto = 0, kGemvDot4 = 1, kGemvMfma = 2 };
 hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
                        const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
-                       void* out, bool out_acc, void* part, size_t part_bytes, GemvKind kind,
+                       void* out, OutKind out_kind, void* part, size_t part_bytes, GemvKind kind,
                        const DeviceInfo& dev, hipStream_t stream);
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceInfo& dev);
 

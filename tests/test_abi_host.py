@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.twl_abi_version() == 2
+    assert lib.twl_abi_version() == 3
 
 
 FAKE = 0x10000   # 16-byte aligned, never dereferenced: every call below fails host validation
@@ -75,6 +75,11 @@ def test_linear_rejects_bad_args(lib):
     # unknown paths
     for path in (-1, 5, 7):
         assert ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 1024, FAKE, 0, path, None, 0, None) == 1
+    # unknown output kinds
+    for kind in (-1, 3):
+        assert ex(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 1024, FAKE, kind, 0, None, 0, None) == 1
+    # bf16 y needs a_scale and smax too
+    assert ex(FAKE, FAKE, FAKE, FAKE, None, 4, 4, 1024, FAKE, 2, 0, None, 0, None) == 1
     # the decode paths (automatic, dot4, MFMA) beyond their batch limit
     for path in (2, 3, 4):
         assert ex(FAKE, FAKE, FAKE, FAKE, FAKE, 25, 4, 1024, FAKE, 0, path, None, 0, None) == 2

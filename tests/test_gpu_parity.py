@@ -271,3 +271,32 @@ def test_repeat_runs_are_bitwise_identical(twl):
         outs.append((host(xi), host(twl.ternary_linear(xi, sc, packed, q, smax))))
     assert np.array_equal(outs[0][0], outs[1][0])
     assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+
+
+# ------------------------------------------------- bf16 output option (R12)
+
+@pytest.mark.parametrize("M,N,K,path", [
+    (300, 513, 2048, "gemm"),            # ragged GEMM tiles, N odd: scalar stores
+    (257, 1024, 3072, "gemm"),           # N % 8 == 0: 16-byte bf16 stores, ragged M
+    (40, 300, 32768, "gemm"),            # GEMM with split-K partials, N % 8 == 4
+    (3, 1000, 5120, "gemv_dot4"),        # dot4 decode
+    (9, 200, 20480, "gemv_mfma"),        # MFMA decode, K split over workgroups
+    (17, 24575, 1024, "gemv_mfma"),      # MFMA decode, row-balanced
+])
+def test_bf16_output(twl, M, N, K, path):
+    # y in bf16 is the fp32 y rounded to nearest even in the epilogue: equal
+    # bit for bit to rounding the kernel's own fp32 y, and within half a bf16
+    # ulp (2^-8 relative) of the oracle's y
+    p = {"gemm": twl.PATH_GEMM, "gemv_dot4": twl.PATH_GEMV_DOT4, "gemv_mfma": twl.PATH_GEMV_MFMA}[path]
+    layer = W.make_layer(4000 + M + N, M, K, N, codes="sparse40")
+    x_i8, a_scale = O.rotate_quant_act(layer.x_bits, layer.sign)
+    packed, q, smax, oq, osm = _check_pack(twl, layer.code, layer.s_bits, "bf16")
+    oy = O.epilogue(O.linear_acc(x_i8, layer.code, oq), a_scale, osm)
+    xi, sc = dev(x_i8), dev(a_scale)
+    announce(f"ternary_linear fp32 and bf16 {path} M={M} N={N} K={K}")
+    y32 = host(twl.ternary_linear(xi, sc, packed, q, smax, path=p))
+    y16 = host(twl.ternary_linear_bf16(xi, sc, packed, q, smax, path=p).view(torch.int16)).view(np.uint16)
+    np.testing.assert_allclose(y32, oy, rtol=Y_RTOL, atol=0)
+    assert np.array_equal(y16, O.round_bf16(y32))
+    y16f = (y16.astype(np.uint32) << 16).view(np.float32)
+    assert np.all(np.abs(y16f.astype(np.float64) - oy) <= 2.0**-8 * np.abs(oy.astype(np.float64)))

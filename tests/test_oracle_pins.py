@@ -358,3 +358,23 @@ def test_negative_control_swapped_sign_blocks_gives_order_one_error():
     bad = np.concatenate([layer.sign[1024:], layer.sign[:1024]])
     x_i8, a_scale = O.rotate_quant_act(layer.x_bits, bad)
     assert O.rel_err(O.ternary_linear(x_i8, a_scale, layer.code, q, smax), ref) > 0.5
+
+
+# ------------------------------------------------------ bf16 output (R12) ---
+
+def test_round_bf16_matches_torch_and_hand_values():
+    # R12: the optional bf16 y is the fp32 y rounded to nearest, ties to even.
+    # Hand values: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 and goes to the
+    # even neighbour 1.0 (0x3F80); 1 + 3 * 2^-8 lies halfway between 1 + 2^-7
+    # (0x3F81, odd) and 1 + 2^-6 (0x3F82) and goes to 0x3F82; -2.75 is exact.
+    hand = np.array([1 + 2.0**-8, 1 + 3 * 2.0**-8, -2.75, 0.0, 3.0e38], dtype=np.float32)
+    assert O.round_bf16(hand).tolist() == [0x3F80, 0x3F82, 0xC030, 0x0000, 0x7F62]
+    # against a library routine: torch's fp32 -> bf16 conversion (round to
+    # nearest even) on random values, exact ties and values near overflow
+    import torch
+    rng = np.random.default_rng(5)
+    v = (rng.standard_normal(200_000) * np.exp(rng.uniform(-30, 30, 200_000))).astype(np.float32)
+    ties = (rng.integers(0, 2**16, 5000).astype(np.uint32) << 16 | np.uint32(0x8000)).view(np.float32)
+    v = np.concatenate([v, ties[np.isfinite(ties)], np.float32([1e-40, -1e-40, 3.38e38])])
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.round_bf16(v), ref)
