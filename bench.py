@@ -223,13 +223,25 @@ def section_layer(torch, twl, name, steps, warmup):
     x, sign, sets = upload_layer(torch, twl, layer, n_copies(layer.N, layer.K))
     ms, rq, lin, lin16 = run_layer_steps(torch, twl, x, sign, sets, steps, warmup, bf16=True)
     ops = 2.0 * layer.M * layer.N * layer.K
+    extra = {}
+    if layer.act == "silu_gate":
+        # the fused SiLU(gate) * up + rotation of this layer's input, from a
+        # [M, 2K] gate/up tensor (random bf16, drawn on the GPU)
+        g = torch.Generator(device="cuda").manual_seed(7)
+        gu = torch.randn((layer.M, 2 * layer.K), generator=g, device="cuda").to(torch.bfloat16)
+        xi = torch.empty((layer.M, layer.K), dtype=torch.int8, device="cuda")
+        sc = torch.empty((layer.M,), dtype=torch.float32, device="cuda")
+        fused = graph_time_ms(torch, lambda: twl.silu_mul_rotate_quant_act(gu, sign, out=(xi, sc)), 50)
+        fb = layer.M * layer.K * 5 + layer.M * 4 + layer.K
+        extra = {"silu_rotq_ms": round(fused, 5), "silu_rotq_gbs": round(fb / fused / 1e6, 1)}
+        del gu
     out = {"M": layer.M, "K": layer.K, "N": layer.N, "ms_per_step": round(ms, 5),
            "step_tops": round(ops / ms / 1e9, 2), "linear_ms": round(lin, 5),
            "linear_tops": round(ops / lin / 1e9, 2),
            "linear_bf16_y_ms": round(lin16, 5), "linear_bf16_y_tops": round(ops / lin16 / 1e9, 2),
            "rotq_ms": round(rq, 5),
            "rotq_gbs": round((layer.M * layer.K * 3 + layer.M * 4 + layer.K) / rq / 1e6, 1),
-           "weight_copies": len(sets)}
+           "weight_copies": len(sets), **extra}
     del sets, x
     torch.cuda.empty_cache()
     return layer, out

@@ -83,6 +83,27 @@ twl_status twl_rotate_quant_act(const uint16_t* x, const int8_t* sign, int64_t M
                                 int8_t* x_i8, float* a_scale, hipStream_t stream);
 
 /*
+ * silu_mul_rotate_quant_act -- the down projection's input step, fused:
+ * rotate_quant_act applied to act = bf16(SiLU(gate) * up), where gate and up
+ * are the two halves of the gate/up projection's output.  [P1] section 1 names
+ * the model's 17408-wide intermediate layer; its gated SiLU activation is this
+ * library's reading, as is the exact evaluation:
+ *   e = exp(-g) by a fixed fp32 sequence (argument clamped to [-87, 88],
+ *       n = rint(x log2 e), r = (x - n * 0x1.62e4p-1) - n * 0x1.7f7d1cp-20,
+ *       Taylor polynomial of degree 7 in Horner form, times 2^n),
+ *   s = g / (1 + e) (IEEE division), act = bf16(s * up) (nearest even),
+ * every step in fp32 without fused multiply-adds, so the result is bit-exact
+ * to an unfused pipeline that evaluates the same steps.
+ *   gate_up in : bf16 bit patterns [M, 2K]; gate = columns 0..K-1, up = K..2K-1
+ *   sign    in : int8 [K]
+ *   x_i8    out: int8 [M, K];  a_scale out: fp32 [M]   (as rotate_quant_act)
+ * Same errors as rotate_quant_act (K % 1024, K <= TWL_MAX_K, alignment).
+ */
+twl_status twl_silu_mul_rotate_quant_act(const uint16_t* gate_up, const int8_t* sign, int64_t M,
+                                         int64_t K, int8_t* x_i8, float* a_scale,
+                                         hipStream_t stream);
+
+/*
  * pack_ternary -- [P1] Prerequisites and section 4 (load time, once per weight).
  *   smax[n]  = max_g |s[n,g]|                               (fp32, exact)
  *   q[n,g]   = rint((127 * s[n,g]) / smax[n])  in fp32, ties to even; 0 if smax = 0

@@ -42,7 +42,16 @@ Readings taken where the pages are silent (each is listed in the design notes):
   epilogue y = acc * a_scale[t] * smax[n] / 127 is evaluated in float64 and
   rounded to fp32 once;  R12 the optional bf16 output is that fp32 y rounded
   to the nearest bf16 value, ties to even (the pages' consumers take bf16
-  activations, [P1] section 4; they do not say how y is narrowed).
+  activations, [P1] section 4; they do not say how y is narrowed);  R13 the
+  down projection's input is SiLU(gate) * up of the gate/up projection's
+  output [M, 2K] (gate = columns 0..K-1), rounded to bf16 as an unfused
+  pipeline would hand it over (the pages name the 27B model's 17408-wide
+  intermediate layer, [P1] section 1, not its activation; SiLU-gated MLPs are
+  the reading);  R14 SiLU is evaluated in fp32 as s = g / (1 + e) with
+  e = exp(-g) from a fixed sequence of fp32 operations (argument clamped to
+  [-87, 88], Cody-Waite reduction by ln 2 split in two, degree-7 Taylor
+  polynomial in Horner form, exact scaling by 2^n), so that two
+  implementations of the method agree bit for bit.
 """
 from __future__ import annotations
 
@@ -283,6 +292,44 @@ def epilogue_at(acc_s: np.ndarray, a_scale: np.ndarray, smax: np.ndarray, rows, 
 def ternary_linear(x_i8, a_scale, code, q, smax):
     """Full prefill/decode linear: int32 acc then the per-token/per-row rescale."""
     return epilogue(linear_acc(x_i8, code, q), a_scale, smax)
+
+
+# ---------------------------------------------------------------------------
+# SiLU(gate) * up feeding the down projection (R13, R14)
+# ---------------------------------------------------------------------------
+
+EXP_LO, EXP_HI = np.float32(-87.0), np.float32(88.0)
+LOG2E = np.float32(1.4426950408889634)
+LN2_HI = np.float32(0.693145751953125)          # 15 significant bits: n * LN2_HI is exact
+LN2_LO = np.float32(0.6931471805599453 - 0.693145751953125)
+EXP_TAYLOR = [np.float32(1.0 / np.prod(np.arange(1, k + 1, dtype=np.float64))) for k in range(8)]
+
+
+def exp_f32(x: np.ndarray) -> np.ndarray:
+    """exp in fp32 by the fixed operation sequence of R14: x = clamp(x),
+    n = rint(x log2 e), r = (x - n ln2_hi) - n ln2_lo, p = sum_k r^k / k!
+    (k <= 7, Horner), exp = p * 2^n."""
+    x = np.clip(np.asarray(x, dtype=np.float32), EXP_LO, EXP_HI)
+    n = np.rint(x * LOG2E)
+    r = (x - n * LN2_HI) - n * LN2_LO
+    p = EXP_TAYLOR[7] * np.ones_like(r)
+    for k in range(6, -1, -1):
+        p = p * r + EXP_TAYLOR[k]
+    return np.ldexp(p, n.astype(np.int32)).astype(np.float32)
+
+
+def silu_mul_bf16(gate_up_bits: np.ndarray) -> np.ndarray:
+    """bf16 [M, 2K] (gate | up) -> bf16 bits [M, K] of SiLU(gate) * up (R13, R14)."""
+    K = gate_up_bits.shape[1] // 2
+    g = bf16_to_f32(gate_up_bits[:, :K])
+    u = bf16_to_f32(gate_up_bits[:, K:])
+    s = g / (np.float32(1.0) + exp_f32(-g))
+    return round_bf16(s * u)
+
+
+def silu_mul_rotate_quant_act(gate_up_bits: np.ndarray, sign: np.ndarray):
+    """The down projection's input step: SiLU(gate) * up, then rotate_quant_act."""
+    return rotate_quant_act(silu_mul_bf16(gate_up_bits), sign)
 
 
 def round_bf16(y: np.ndarray) -> np.ndarray:

@@ -20,7 +20,7 @@ from ._lib import (GEMV_MAX_M, GROUP, HBLOCK, MAX_K, PATH_AUTO, PATH_GEMM, PATH_
                    PATH_GEMV_MFMA, TwlError)
 
 __all__ = [
-    "rotate_quant_act", "pack_ternary", "ternary_linear", "ternary_linear_acc", "ternary_linear_bf16",
+    "rotate_quant_act", "silu_mul_rotate_quant_act", "pack_ternary", "ternary_linear", "ternary_linear_acc", "ternary_linear_bf16",
     "workspace_bytes", "packed_bytes", "TwlError", "PATH_AUTO", "PATH_GEMM", "PATH_GEMV", "PATH_GEMV_DOT4",
     "PATH_GEMV_MFMA", "GEMV_MAX_M",
     "HBLOCK", "GROUP", "MAX_K", "library",
@@ -71,6 +71,28 @@ def rotate_quant_act(x, sign, out: Optional[Tuple] = None, stream=None):
         M, K, _dev_ptr(x_i8, "x_i8", (torch.int8,)), _dev_ptr(a_scale, "a_scale", (torch.float32,)),
         _stream_handle(stream))
     _lib.check(st, "twl_rotate_quant_act")
+    return x_i8, a_scale
+
+
+def silu_mul_rotate_quant_act(gate_up, sign, out: Optional[Tuple] = None, stream=None):
+    """gate_up [M, 2K] bf16 (gate | up), sign [K] int8 -> (x_i8, a_scale) of
+    rotate_quant_act applied to bf16(SiLU(gate) * up)."""
+    torch = _torch()
+    lib = _lib.load()
+    M, K2 = gate_up.shape
+    if K2 % 2:
+        raise ValueError(f"gate_up has {K2} columns, expected 2K")
+    K = K2 // 2
+    if out is None:
+        x_i8 = torch.empty((M, K), dtype=torch.int8, device=gate_up.device)
+        a_scale = torch.empty((M,), dtype=torch.float32, device=gate_up.device)
+    else:
+        x_i8, a_scale = out
+    st = lib.twl_silu_mul_rotate_quant_act(
+        _dev_ptr(gate_up, "gate_up", (torch.bfloat16, torch.int16)), _dev_ptr(sign, "sign", (torch.int8,)),
+        M, K, _dev_ptr(x_i8, "x_i8", (torch.int8,)), _dev_ptr(a_scale, "a_scale", (torch.float32,)),
+        _stream_handle(stream))
+    _lib.check(st, "twl_silu_mul_rotate_quant_act")
     return x_i8, a_scale
 
 

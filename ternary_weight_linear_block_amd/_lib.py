@@ -25,6 +25,7 @@ _SIZE = ctypes.c_size_t
 _INT = ctypes.c_int
 SIGNATURES = [
     ("twl_rotate_quant_act", _INT, [_P, _P, _I64, _I64, _P, _P, _P]),
+    ("twl_silu_mul_rotate_quant_act", _INT, [_P, _P, _I64, _I64, _P, _P, _P]),
     ("twl_pack_ternary", _INT, [_P, _P, _I64, _I64, _P, _P, _P, _P, _P]),
     ("twl_packed_bytes", _SIZE, [_I64, _I64]),
     ("twl_workspace_bytes", _SIZE, [_I64, _I64, _I64]),

@@ -123,6 +123,22 @@ twl_status twl_rotate_quant_act(const uint16_t* x, const int8_t* sign, int64_t M
                   "rotate_quant_act");
 }
 
+twl_status twl_silu_mul_rotate_quant_act(const uint16_t* gate_up, const int8_t* sign, int64_t M,
+                                         int64_t K, int8_t* x_i8, float* a_scale,
+                                         hipStream_t stream) {
+  TWL_TRY(check_rows("M", M));
+  TWL_TRY(check_k(K));
+  if (M == 0) return ok();
+  TWL_REQUIRE_PTR(gate_up);
+  TWL_REQUIRE_PTR(sign);
+  TWL_REQUIRE_PTR(x_i8);
+  TWL_REQUIRE_PTR(a_scale);
+  twl::DeviceInfo dev;
+  TWL_TRY(current_device(&dev));
+  return launched(twl::launch_silu_mul_rotate_quant(gate_up, sign, M, K, x_i8, a_scale, stream),
+                  "silu_mul_rotate_quant_act");
+}
+
 twl_status twl_pack_ternary(const int8_t* code, const uint16_t* s, int64_t N, int64_t K,
                             uint8_t* packed, int8_t* q, float* smax, int32_t* bad_codes,
                             hipStream_t stream) {

@@ -38,6 +38,39 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
+// exp(x) in fp32 by a fixed sequence of operations, so that any two
+// implementations of the fused activation agree bit for bit: clamp to
+// [-87, 88] (e^x stays a normal float and 1 + e^-x is then exact or finite),
+// n = rint(x log2 e), Cody-Waite reduction r = (x - n ln2_hi) - n ln2_lo with
+// ln2_hi = 0x1.62e4p-1 (15 significant bits, so n ln2_hi is exact), the
+// Taylor polynomial of degree 7 (coefficients 1/k! rounded to fp32) in Horner
+// form, and exact scaling by 2^n.  Within 1.2 ulp of exp over the range.
+// No operation may be fused (the library is built with -ffp-contract=off).
+__device__ __forceinline__ float exp_fixed(float x) {
+  x = fminf(fmaxf(x, -87.0f), 88.0f);
+  const float n = rintf(x * 0x1.715476p+0f);
+  const float r = (x - n * 0x1.62e4p-1f) - n * 0x1.7f7d1cp-20f;
+  float p = 0x1.a01a02p-13f;  // 1/7!
+  p = p * r + 0x1.6c16c2p-10f;  // 1/6!
+  p = p * r + 0x1.111112p-7f;   // 1/5!
+  p = p * r + 0x1.555556p-5f;   // 1/4!
+  p = p * r + 0x1.555556p-3f;   // 1/3!
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  return ldexpf(p, static_cast<int>(n));
+}
+
+// bf16 bits of SiLU(g) * u for bf16 inputs g and u: s = g / (1 + exp(-g)) and
+// s * u in fp32, rounded to bf16 (nearest even) as an unfused activation step
+// would store it.
+__device__ __forceinline__ uint32_t silu_mul_bits(uint32_t g_bits, uint32_t u_bits) {
+  const float g = bf16_bits_to_float(g_bits);
+  const float u = bf16_bits_to_float(u_bits);
+  const float s = g / (1.0f + exp_fixed(-g));  // IEEE division
+  return f32_to_bf16_rne(s * u);
+}
+
 // The butterflies of stage h = 2^b on register slot bit `sb` of a 16-slot
 // lane: slot j (bit sb clear) holds the lower position, j | (1 << sb) the
 // upper one.
@@ -69,7 +102,9 @@ __device__ __forceinline__ void lds_wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int BPW>
+// SILU: x is the gate/up output [M, 2K] (gate = columns 0..K-1) and the
+// rotated input is bf16(SiLU(gate) * up), computed as the block is loaded.
+template <int BPW, bool SILU>
 __global__ __launch_bounds__(1024) void rotate_quant_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ sign, int K, int nblocks,
     int8_t* __restrict__ x_i8, float* __restrict__ a_scale) {
@@ -78,7 +113,7 @@ __global__ __launch_bounds__(1024) void rotate_quant_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-  const uint16_t* xr = x + static_cast<size_t>(t) * K;
+  const uint16_t* xr = x + static_cast<size_t>(t) * (SILU ? 2 * K : K);
   float* wb = wbuf_all + wave * kWaveBufWords;
   // layout-1 lane bits: e[9:8] = lane >> 4, e[3:0] = lane & 15;
   // layout-2 lane bits: e[7:2] = lane
@@ -96,7 +131,16 @@ __global__ __launch_bounds__(1024) void rotate_quant_kernel(
       const uint4 p0 = *reinterpret_cast<const uint4*>(xr + k0);
       const uint4 p1 = *reinterpret_cast<const uint4*>(xr + k0 + 8);
       const uint4 sg = *reinterpret_cast<const uint4*>(sign + k0);
-      const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+      uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+      if (SILU) {
+        const uint4 u0 = *reinterpret_cast<const uint4*>(xr + K + k0);
+        const uint4 u1 = *reinterpret_cast<const uint4*>(xr + K + k0 + 8);
+        const uint32_t uw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pw[e] = silu_mul_bits(pw[e] & 0xFFFFu, uw[e] & 0xFFFFu) |
+                  (silu_mul_bits(pw[e] >> 16, uw[e] >> 16) << 16);
+      }
       const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
       float(&w)[16] = v[i];
 #pragma unroll
@@ -181,7 +225,7 @@ __global__ __launch_bounds__(1024) void rotate_quant_kernel(
   }
 }
 
-template <int BPW>
+template <int BPW, bool SILU>
 hipError_t launch_bpw(const uint16_t* x, const int8_t* sign, int64_t M, int64_t K,
                       int8_t* x_i8, float* a_scale, hipStream_t stream) {
   const int nblocks = static_cast<int>(K / kBlock);
@@ -189,26 +233,38 @@ hipError_t launch_bpw(const uint16_t* x, const int8_t* sign, int64_t M, int64_t 
   const size_t lds = static_cast<size_t>(nw) * kWaveBufWords * sizeof(float);
   if (lds > 65536) {
     // more than the default dynamic LDS limit: the part has 160 KiB per CU
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(rotate_quant_kernel<BPW>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(rotate_quant_kernel<BPW, SILU>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(rotate_quant_kernel<BPW>, dim3(static_cast<unsigned>(M)), dim3(64 * nw),
+  hipLaunchKernelGGL((rotate_quant_kernel<BPW, SILU>), dim3(static_cast<unsigned>(M)), dim3(64 * nw),
                      lds, stream, x, sign,
                      static_cast<int>(K), nblocks, x_i8, a_scale);
   return hipGetLastError();
+}
+
+template <bool SILU>
+hipError_t launch_rotate(const uint16_t* x, const int8_t* sign, int64_t M, int64_t K,
+                         int8_t* x_i8, float* a_scale, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const int64_t nblocks = K / kBlock;  // 1 .. 64 (validated by the caller)
+  if (nblocks <= 16) return launch_bpw<1, SILU>(x, sign, M, K, x_i8, a_scale, stream);
+  if (nblocks <= 32) return launch_bpw<2, SILU>(x, sign, M, K, x_i8, a_scale, stream);
+  return launch_bpw<4, SILU>(x, sign, M, K, x_i8, a_scale, stream);
 }
 
 }  // namespace
 
 hipError_t launch_rotate_quant(const uint16_t* x, const int8_t* sign, int64_t M, int64_t K,
                                int8_t* x_i8, float* a_scale, hipStream_t stream) {
-  if (M == 0) return hipSuccess;
-  const int64_t nblocks = K / kBlock;  // 1 .. 64 (validated by the caller)
-  if (nblocks <= 16) return launch_bpw<1>(x, sign, M, K, x_i8, a_scale, stream);
-  if (nblocks <= 32) return launch_bpw<2>(x, sign, M, K, x_i8, a_scale, stream);
-  return launch_bpw<4>(x, sign, M, K, x_i8, a_scale, stream);
+  return launch_rotate<false>(x, sign, M, K, x_i8, a_scale, stream);
+}
+
+hipError_t launch_silu_mul_rotate_quant(const uint16_t* gate_up, const int8_t* sign, int64_t M,
+                                        int64_t K, int8_t* x_i8, float* a_scale,
+                                        hipStream_t stream) {
+  return launch_rotate<true>(gate_up, sign, M, K, x_i8, a_scale, stream);
 }
 
 }  // namespace twl

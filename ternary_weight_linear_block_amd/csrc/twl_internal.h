@@ -16,6 +16,10 @@ struct DeviceInfo {
 
 hipError_t launch_rotate_quant(const uint16_t* x, const int8_t* sign, int64_t M, int64_t K,
                                int8_t* x_i8, float* a_scale, hipStream_t stream);
+// gate_up: bf16 [M, 2K]; rotates bf16(SiLU(gate) * up).
+hipError_t launch_silu_mul_rotate_quant(const uint16_t* gate_up, const int8_t* sign, int64_t M,
+                                        int64_t K, int8_t* x_i8, float* a_scale,
+                                        hipStream_t stream);
 
 hipError_t launch_pack(const int8_t* code, const uint16_t* s, int64_t N, int64_t K,
                        uint8_t* packed, int8_t* q, float* smax, int32_t* bad_codes,

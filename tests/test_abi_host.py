@@ -64,6 +64,14 @@ def test_rotate_rejects_null_and_misaligned(lib):
     assert lib.twl_rotate_quant_act(FAKE, FAKE, -1, 1024, FAKE, FAKE, None) == 1
 
 
+def test_fused_activation_rejects_bad_args(lib):
+    f = lib.twl_silu_mul_rotate_quant_act
+    assert f(FAKE, FAKE, 4, 1000, FAKE, FAKE, None) == 2
+    assert f(None, FAKE, 4, 1024, FAKE, FAKE, None) == 1
+    assert f(FAKE + 2, FAKE, 4, 1024, FAKE, FAKE, None) == 3
+    assert f(None, None, 0, 1024, None, None, None) == 0
+
+
 def test_pack_rejects_bad_args(lib):
     assert lib.twl_pack_ternary(FAKE, FAKE, 8, 1000, FAKE, FAKE, FAKE, None, None) == 2
     assert lib.twl_pack_ternary(FAKE, None, 8, 1024, FAKE, FAKE, FAKE, None, None) == 1

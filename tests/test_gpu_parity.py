@@ -300,3 +300,38 @@ def test_bf16_output(twl, M, N, K, path):
     assert np.array_equal(y16, O.round_bf16(y32))
     y16f = (y16.astype(np.uint32) << 16).view(np.float32)
     assert np.all(np.abs(y16f.astype(np.float64) - oy) <= 2.0**-8 * np.abs(oy.astype(np.float64)))
+
+
+# ------------------------------- fused SiLU(gate) * up rotation (R13, R14)
+
+@pytest.mark.parametrize("M,K", [(256, 17408), (1, 17408), (24, 17408), (7, 5120), (3, 65536)])
+def test_silu_mul_rotate_quant_act(twl, M, K):
+    gu, sign = W.make_gate_up(5000 + M + K, M, K)
+    announce(f"silu_mul_rotate_quant_act M={M} K={K}")
+    xi, sc = twl.silu_mul_rotate_quant_act(dev(gu.view(np.int16)), dev(sign))
+    ox, osc = O.silu_mul_rotate_quant_act(gu, sign)
+    assert np.array_equal(host(sc).view(np.uint32), osc.view(np.uint32))
+    bad = np.argwhere(host(xi) != ox)
+    assert bad.size == 0, f"{len(bad)} x_i8 mismatches, first {bad[:5].tolist()}"
+
+
+def test_silu_mul_rotate_edge_values(twl):
+    # the clamp of exp's argument (|gate| > 87), zeros, and tokens whose
+    # activation is all zero (a_scale = 0)
+    K = 2048
+    g = np.zeros((4, K), dtype=np.float32)
+    u = np.ones((4, K), dtype=np.float32)
+    g[0] = np.linspace(-300, 300, K)
+    g[1] = -120.0
+    u[1] = 1e30
+    g[2] = 0.0                      # SiLU(0) = 0: zero token
+    g[3] = np.linspace(-4, 4, K)
+    u[3, ::2] = 0.0
+    gu = np.concatenate([W.f32_to_bf16_bits(g), W.f32_to_bf16_bits(u)], axis=1)
+    sign = np.where(np.arange(K) % 5 == 0, -1, 1).astype(np.int8)
+    announce("silu_mul_rotate_quant_act edge values")
+    xi, sc = twl.silu_mul_rotate_quant_act(dev(gu.view(np.int16)), dev(sign))
+    ox, osc = O.silu_mul_rotate_quant_act(gu, sign)
+    assert np.array_equal(host(sc).view(np.uint32), osc.view(np.uint32))
+    assert np.array_equal(host(xi), ox)
+    assert osc[2] == 0

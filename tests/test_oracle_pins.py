@@ -378,3 +378,50 @@ def test_round_bf16_matches_torch_and_hand_values():
     v = np.concatenate([v, ties[np.isfinite(ties)], np.float32([1e-40, -1e-40, 3.38e38])])
     ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(O.round_bf16(v), ref)
+
+
+# ------------------------------------- fused SiLU(gate) * up (R13, R14) -----
+
+def test_exp_f32_is_within_1_25_ulp_of_exp():
+    # R14's fixed fp32 exp against the mathematical function (float64 exp)
+    x = np.linspace(-87.0, 88.0, 1_000_001, dtype=np.float32)
+    x = np.concatenate([x, np.float32([0.0, -0.0, 1e-30, -1e-30, 0.5, -0.5])])
+    e = O.exp_f32(x).astype(np.float64)
+    t = np.exp(x.astype(np.float64))
+    ulp = np.spacing(t.astype(np.float32)).astype(np.float64)
+    assert np.max(np.abs(e - t) / ulp) <= 1.25
+    assert O.exp_f32(np.float32([0.0]))[0] == 1.0
+    # the clamp: far outside the range the value of the end point is used
+    assert O.exp_f32(np.float32([-200.0]))[0] == O.exp_f32(np.float32([-87.0]))[0]
+    assert O.exp_f32(np.float32([200.0]))[0] == O.exp_f32(np.float32([88.0]))[0]
+
+
+def _bf16(v):
+    return W.f32_to_bf16_bits(np.asarray(v, dtype=np.float32))
+
+
+def test_silu_mul_hand_values():
+    # worked by hand: SiLU(1) = 1 / (1 + e^-1) = 0.731058..., bf16 0.73046875
+    # (0x3F3B); SiLU(-1) * 2 = -0.537883..., bf16 -0.5390625 (0xBF0A); SiLU(0) = 0
+    gu = np.concatenate([_bf16([[1.0, -1.0, 0.0, 3.0]]), _bf16([[1.0, 2.0, 5.0, 0.0]])], axis=1)
+    assert O.silu_mul_bf16(gu).tolist() == [[0x3F3B, 0xBF0A, 0x0000, 0x0000]]
+
+
+def test_silu_mul_matches_float64_within_bf16_rounding():
+    gu, _ = W.make_gate_up(11, 64, 1024)
+    act = O.bf16_to_f32(O.silu_mul_bf16(gu)).astype(np.float64)
+    g = O.bf16_to_f32(gu[:, :1024]).astype(np.float64)
+    u = O.bf16_to_f32(gu[:, 1024:]).astype(np.float64)
+    exact = g / (1.0 + np.exp(-g)) * u
+    # half a bf16 ulp (at most 2^-8 relative) plus the fp32 steps before the
+    # rounding; and most values much closer than the bound
+    err = np.abs(act - exact)
+    assert np.all(err <= (2.0**-8 + 2.0**-20) * np.abs(exact) + 1e-30)
+    assert np.median(err / np.maximum(np.abs(exact), 1e-30)) < 2.0**-9
+
+
+def test_fused_step_equals_activation_then_rotation():
+    gu, sign = W.make_gate_up(12, 8, 2048)
+    xi, sc = O.silu_mul_rotate_quant_act(gu, sign)
+    xi2, sc2 = O.rotate_quant_act(O.silu_mul_bf16(gu), sign)
+    assert np.array_equal(xi, xi2) and np.array_equal(sc, sc2)

@@ -98,6 +98,17 @@ def draw_activations(rng: np.random.Generator, M: int, K: int, act: str) -> np.n
     return f32_to_bf16_bits(x)
 
 
+def make_gate_up(seed: int, M: int, K: int):
+    """Raw input of the down projection's fused activation step: bf16 bit
+    patterns [M, 2K] holding gate (columns 0..K-1) and up (K..2K-1), both
+    N(0,1), and a sign table of width K.  No activation is applied here."""
+    if K % HBLOCK:
+        raise ValueError("K must be a multiple of 1024")
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((M, 2 * K), dtype=np.float32)
+    return f32_to_bf16_bits(g), draw_sign(rng, K)
+
+
 def draw_sign(rng: np.random.Generator, K: int) -> np.ndarray:
     return rng.choice(np.array([-1, 1], dtype=np.int8), size=K)
 
