@@ -218,12 +218,26 @@ def copy_calibration(torch) -> int:
 
 
 def section_layer(torch, twl, name, steps, warmup):
+    import numpy as np
     import workloads as W
     layer = W.make_config(name)
     x, sign, sets = upload_layer(torch, twl, layer, n_copies(layer.N, layer.K))
     ms, rq, lin, lin16 = run_layer_steps(torch, twl, x, sign, sets, steps, warmup, bf16=True)
     ops = 2.0 * layer.M * layer.N * layer.K
     extra = {}
+    if name == "prefill_gate_up":
+        # the bf16 reference path ([P1] section 4's pre-int8 path) on the same
+        # layer: the rotation to bf16, then the exact-dequant bf16 MFMA kernel
+        # (one weight copy: this is an A/B point, not the hot path)
+        s_d = torch.from_numpy(layer.s_bits.view(np.int16)).cuda()
+        packed0 = sets[0][0]
+        r = twl.rotate_act_bf16(x, sign)
+        yr = torch.empty((layer.M, layer.N), dtype=torch.float32, device="cuda")
+        rot_ms = graph_time_ms(torch, lambda: twl.rotate_act_bf16(x, sign, out=r), 20)
+        ref_ms = graph_time_ms(torch, lambda: twl.reference_linear_bf16(r, packed0, s_d, out=yr), 5)
+        extra = {"reference_bf16_rotate_ms": round(rot_ms, 5), "reference_bf16_linear_ms": round(ref_ms, 5),
+                 "reference_bf16_tflops": round(ops / ref_ms / 1e9, 2)}
+        del r, yr, s_d
     if layer.act == "silu_gate":
         # the fused SiLU(gate) * up + rotation of this layer's input, from a
         # [M, 2K] gate/up tensor (random bf16, drawn on the GPU)

@@ -166,6 +166,31 @@ twl_status twl_ternary_linear_acc(const int8_t* x_i8, const uint8_t* packed, con
                                   int64_t M, int64_t N, int64_t K, int32_t* acc,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * rotate_act_bf16 -- the rotation of rotate_quant_act alone (same sign and
+ * block FWHT, same fp32 operations), without the int8 step: r rounded to bf16
+ * (nearest even).  The input of the bf16 reference linear below.
+ *   x in: bf16 bit patterns [M, K];  sign in: int8 [K];  r out: bf16 bits [M, K]
+ */
+twl_status twl_rotate_act_bf16(const uint16_t* x, const int8_t* sign, int64_t M, int64_t K,
+                               uint16_t* r, hipStream_t stream);
+
+/*
+ * reference_linear_bf16 -- [P1] section 4, the bf16 path the int8 GEMM
+ * replaced (kept as an accuracy reference and an A/B point):
+ *   y[t,n] = sum_k r[t,k] * code[n,k] * bf16(s[n, k/128])    (fp32 accumulation)
+ * with the weights expanded from the packed codes and the ORIGINAL fp16 scales
+ * in registers (s rounded to bf16, nearest even).  Not the hot path: no
+ * workspace, no split-K, one untuned kernel.
+ *   r      in : bf16 bit patterns [M, K] (from twl_rotate_act_bf16)
+ *   packed in : twl_packed_bytes(N, K) bytes (from twl_pack_ternary)
+ *   s      in : fp16 bit patterns [N, K/128]
+ *   y      out: fp32 [M, N]
+ */
+twl_status twl_reference_linear_bf16(const uint16_t* r, const uint8_t* packed, const uint16_t* s,
+                                     int64_t M, int64_t N, int64_t K, float* y,
+                                     hipStream_t stream);
+
 /* What twl_ternary_linear_ex writes into `out` [M, N]. */
 typedef enum {
   TWL_OUT_F32 = 0,      /* y, fp32                                              */

@@ -51,7 +51,12 @@ Readings taken where the pages are silent (each is listed in the design notes):
   e = exp(-g) from a fixed sequence of fp32 operations (argument clamped to
   [-87, 88], Cody-Waite reduction by ln 2 split in two, degree-7 Taylor
   polynomial in Horner form, exact scaling by 2^n), so that two
-  implementations of the method agree bit for bit.
+  implementations of the method agree bit for bit;  R15 the bf16 reference
+  path ([P1] section 4's pre-int8 path) uses the rotated activation rounded to
+  bf16 and the weights code * bf16(s) (the fp16 scale rounded to bf16), with
+  fp32 accumulation on the GPU; the oracle sums the exact products in
+  float64, and the GPU is held to the fp32 accumulation bound
+  K * 2^-24 * sum_k |r W| per output.
 """
 from __future__ import annotations
 
@@ -330,6 +335,31 @@ def silu_mul_bf16(gate_up_bits: np.ndarray) -> np.ndarray:
 def silu_mul_rotate_quant_act(gate_up_bits: np.ndarray, sign: np.ndarray):
     """The down projection's input step: SiLU(gate) * up, then rotate_quant_act."""
     return rotate_quant_act(silu_mul_bf16(gate_up_bits), sign)
+
+
+# ---------------------------------------------------------------------------
+# bf16 reference path ([P1] section 4's pre-int8 path; R15)
+# ---------------------------------------------------------------------------
+
+def rotate_bf16(x_bits: np.ndarray, sign: np.ndarray) -> np.ndarray:
+    """The rotation of rotate_quant_act, r rounded to bf16 bits [M, K]."""
+    return round_bf16(rotate(x_bits, sign))
+
+
+def dequant_bf16(code: np.ndarray, s_bits: np.ndarray) -> np.ndarray:
+    """W[n,k] = code[n,k] * bf16(s[n, k/128]) as float64 [N, K] (exact values)."""
+    s32 = s_bits.view(np.float16).astype(np.float32)
+    sb = bf16_to_f32(round_bf16(s32)).astype(np.float64)
+    return np.asarray(code, dtype=np.float64) * np.repeat(sb, GROUP, axis=1)
+
+
+def reference_linear_bf16(r_bits: np.ndarray, code: np.ndarray, s_bits: np.ndarray):
+    """y = r . W^T with the exact products summed in float64; returns (y as
+    float64, sum_k |r W| as float64) -- the second is the scale of the GPU's
+    fp32 accumulation bound (R15)."""
+    r = bf16_to_f32(r_bits).astype(np.float64)
+    w = dequant_bf16(code, s_bits)
+    return r @ w.T, np.abs(r) @ np.abs(w).T
 
 
 def round_bf16(y: np.ndarray) -> np.ndarray:

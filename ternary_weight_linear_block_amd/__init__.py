@@ -20,7 +20,8 @@ from ._lib import (GEMV_MAX_M, GROUP, HBLOCK, MAX_K, PATH_AUTO, PATH_GEMM, PATH_
                    PATH_GEMV_MFMA, TwlError)
 
 __all__ = [
-    "rotate_quant_act", "silu_mul_rotate_quant_act", "pack_ternary", "ternary_linear", "ternary_linear_acc", "ternary_linear_bf16",
+    "rotate_quant_act", "silu_mul_rotate_quant_act", "pack_ternary", "rotate_act_bf16",
+    "reference_linear_bf16", "ternary_linear", "ternary_linear_acc", "ternary_linear_bf16",
     "workspace_bytes", "packed_bytes", "TwlError", "PATH_AUTO", "PATH_GEMM", "PATH_GEMV", "PATH_GEMV_DOT4",
     "PATH_GEMV_MFMA", "GEMV_MAX_M",
     "HBLOCK", "GROUP", "MAX_K", "library",
@@ -94,6 +95,41 @@ def silu_mul_rotate_quant_act(gate_up, sign, out: Optional[Tuple] = None, stream
         _stream_handle(stream))
     _lib.check(st, "twl_silu_mul_rotate_quant_act")
     return x_i8, a_scale
+
+
+def rotate_act_bf16(x, sign, out=None, stream=None):
+    """x [M, K] bf16, sign [K] int8 -> r [M, K] bf16: the rotation alone."""
+    torch = _torch()
+    lib = _lib.load()
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
+    st = lib.twl_rotate_act_bf16(
+        _dev_ptr(x, "x", (torch.bfloat16, torch.int16)), _dev_ptr(sign, "sign", (torch.int8,)),
+        M, K, _dev_ptr(out, "r", (torch.bfloat16, torch.int16)), _stream_handle(stream))
+    _lib.check(st, "twl_rotate_act_bf16")
+    return out
+
+
+def reference_linear_bf16(r, packed, s, out=None, stream=None):
+    """r [M, K] bf16 (rotate_act_bf16), packed (pack_ternary), s [N, K/128] fp16
+    -> y [M, N] fp32 = r . (code * bf16(s))^T, the bf16 reference path."""
+    torch = _torch()
+    lib = _lib.load()
+    M, K = r.shape
+    N = s.shape[0]
+    if s.dim() != 2 or s.shape[1] * GROUP != K:
+        raise ValueError(f"s has shape {tuple(s.shape)}, expected [N, K/128] with K = {K}")
+    if N > 0 and packed.numel() != packed_bytes(N, K):
+        raise ValueError(f"packed has {packed.numel()} bytes, expected {packed_bytes(N, K)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=r.device)
+    st = lib.twl_reference_linear_bf16(
+        _dev_ptr(r, "r", (torch.bfloat16, torch.int16)), _dev_ptr(packed, "packed", (torch.uint8,)),
+        _dev_ptr(s, "s", (torch.float16, torch.int16)), M, N, K,
+        _dev_ptr(out, "y", (torch.float32,)), _stream_handle(stream))
+    _lib.check(st, "twl_reference_linear_bf16")
+    return out
 
 
 def packed_bytes(N: int, K: int) -> int:

@@ -26,6 +26,8 @@ _INT = ctypes.c_int
 SIGNATURES = [
     ("twl_rotate_quant_act", _INT, [_P, _P, _I64, _I64, _P, _P, _P]),
     ("twl_silu_mul_rotate_quant_act", _INT, [_P, _P, _I64, _I64, _P, _P, _P]),
+    ("twl_rotate_act_bf16", _INT, [_P, _P, _I64, _I64, _P, _P]),
+    ("twl_reference_linear_bf16", _INT, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
     ("twl_pack_ternary", _INT, [_P, _P, _I64, _I64, _P, _P, _P, _P, _P]),
     ("twl_packed_bytes", _SIZE, [_I64, _I64]),
     ("twl_workspace_bytes", _SIZE, [_I64, _I64, _I64]),

@@ -23,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libtwl.so")
 
-SOURCES = ["rotate_quant.hip", "pack.hip", "gemm_i8.hip", "gemv.hip", "api.cpp"]
+SOURCES = ["rotate_quant.hip", "pack.hip", "gemm_i8.hip", "gemv.hip", "reference_bf16.hip", "api.cpp"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

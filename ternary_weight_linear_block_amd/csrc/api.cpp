@@ -139,6 +139,36 @@ twl_status twl_silu_mul_rotate_quant_act(const uint16_t* gate_up, const int8_t* 
                   "silu_mul_rotate_quant_act");
 }
 
+twl_status twl_rotate_act_bf16(const uint16_t* x, const int8_t* sign, int64_t M, int64_t K,
+                               uint16_t* r, hipStream_t stream) {
+  TWL_TRY(check_rows("M", M));
+  TWL_TRY(check_k(K));
+  if (M == 0) return ok();
+  TWL_REQUIRE_PTR(x);
+  TWL_REQUIRE_PTR(sign);
+  TWL_REQUIRE_PTR(r);
+  twl::DeviceInfo dev;
+  TWL_TRY(current_device(&dev));
+  return launched(twl::launch_rotate_bf16(x, sign, M, K, r, stream), "rotate_act_bf16");
+}
+
+twl_status twl_reference_linear_bf16(const uint16_t* r, const uint8_t* packed, const uint16_t* s,
+                                     int64_t M, int64_t N, int64_t K, float* y,
+                                     hipStream_t stream) {
+  TWL_TRY(check_rows("M", M));
+  TWL_TRY(check_rows("N", N));
+  TWL_TRY(check_k(K));
+  if (M == 0 || N == 0) return ok();
+  TWL_REQUIRE_PTR(r);
+  TWL_REQUIRE_PTR(packed);
+  TWL_REQUIRE_PTR(s);
+  TWL_REQUIRE_PTR(y);
+  twl::DeviceInfo dev;
+  TWL_TRY(current_device(&dev));
+  return launched(twl::launch_reference_bf16(r, packed, s, M, N, K, y, stream),
+                  "reference_linear_bf16");
+}
+
 twl_status twl_pack_ternary(const int8_t* code, const uint16_t* s, int64_t N, int64_t K,
                             uint8_t* packed, int8_t* q, float* smax, int32_t* bad_codes,
                             hipStream_t stream) {

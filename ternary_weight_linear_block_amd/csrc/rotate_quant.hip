@@ -104,7 +104,9 @@ __device__ __forceinline__ void lds_wave_sync() {
 
 // SILU: x is the gate/up output [M, 2K] (gate = columns 0..K-1) and the
 // rotated input is bf16(SiLU(gate) * up), computed as the block is loaded.
-template <int BPW, bool SILU>
+// RAW: no quantisation; r itself is written as bf16 (nearest even) to
+// `x_i8`, which then points to uint16 [M, K], and a_scale is not touched.
+template <int BPW, bool SILU, bool RAW>
 __global__ __launch_bounds__(1024) void rotate_quant_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ sign, int K, int nblocks,
     int8_t* __restrict__ x_i8, float* __restrict__ a_scale) {
@@ -186,8 +188,18 @@ __global__ __launch_bounds__(1024) void rotate_quant_kernel(
         w[e] *= 0.03125f;  // orthonormal 1/sqrt(1024): exact power of two
         amax = fmaxf(amax, fabsf(w[e]));
       }
+      if (RAW) {
+        uint16_t* rr = reinterpret_cast<uint16_t*>(x_i8) + static_cast<size_t>(t) * K + b * kBlock;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t lo = f32_to_bf16_rne(w[4 * c]) | (static_cast<uint32_t>(f32_to_bf16_rne(w[4 * c + 1])) << 16);
+          const uint32_t hi = f32_to_bf16_rne(w[4 * c + 2]) | (static_cast<uint32_t>(f32_to_bf16_rne(w[4 * c + 3])) << 16);
+          *reinterpret_cast<uint2*>(rr + 256 * c + 4 * lane) = make_uint2(lo, hi);
+        }
+      }
     }
   }
+  if (RAW) return;
 
   // per-token absmax over the whole row: lanes, then waves
 #pragma unroll
@@ -225,7 +237,7 @@ __global__ __launch_bounds__(1024) void rotate_quant_kernel(
   }
 }
 
-template <int BPW, bool SILU>
+template <int BPW, bool SILU, bool RAW>
 hipError_t launch_bpw(const uint16_t* x, const int8_t* sign, int64_t M, int64_t K,
                       int8_t* x_i8, float* a_scale, hipStream_t stream) {
   const int nblocks = static_cast<int>(K / kBlock);
@@ -233,38 +245,43 @@ hipError_t launch_bpw(const uint16_t* x, const int8_t* sign, int64_t M, int64_t 
   const size_t lds = static_cast<size_t>(nw) * kWaveBufWords * sizeof(float);
   if (lds > 65536) {
     // more than the default dynamic LDS limit: the part has 160 KiB per CU
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(rotate_quant_kernel<BPW, SILU>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(rotate_quant_kernel<BPW, SILU, RAW>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((rotate_quant_kernel<BPW, SILU>), dim3(static_cast<unsigned>(M)), dim3(64 * nw),
+  hipLaunchKernelGGL((rotate_quant_kernel<BPW, SILU, RAW>), dim3(static_cast<unsigned>(M)), dim3(64 * nw),
                      lds, stream, x, sign,
                      static_cast<int>(K), nblocks, x_i8, a_scale);
   return hipGetLastError();
 }
 
-template <bool SILU>
+template <bool SILU, bool RAW>
 hipError_t launch_rotate(const uint16_t* x, const int8_t* sign, int64_t M, int64_t K,
                          int8_t* x_i8, float* a_scale, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const int64_t nblocks = K / kBlock;  // 1 .. 64 (validated by the caller)
-  if (nblocks <= 16) return launch_bpw<1, SILU>(x, sign, M, K, x_i8, a_scale, stream);
-  if (nblocks <= 32) return launch_bpw<2, SILU>(x, sign, M, K, x_i8, a_scale, stream);
-  return launch_bpw<4, SILU>(x, sign, M, K, x_i8, a_scale, stream);
+  if (nblocks <= 16) return launch_bpw<1, SILU, RAW>(x, sign, M, K, x_i8, a_scale, stream);
+  if (nblocks <= 32) return launch_bpw<2, SILU, RAW>(x, sign, M, K, x_i8, a_scale, stream);
+  return launch_bpw<4, SILU, RAW>(x, sign, M, K, x_i8, a_scale, stream);
 }
 
 }  // namespace
 
 hipError_t launch_rotate_quant(const uint16_t* x, const int8_t* sign, int64_t M, int64_t K,
                                int8_t* x_i8, float* a_scale, hipStream_t stream) {
-  return launch_rotate<false>(x, sign, M, K, x_i8, a_scale, stream);
+  return launch_rotate<false, false>(x, sign, M, K, x_i8, a_scale, stream);
 }
 
 hipError_t launch_silu_mul_rotate_quant(const uint16_t* gate_up, const int8_t* sign, int64_t M,
                                         int64_t K, int8_t* x_i8, float* a_scale,
                                         hipStream_t stream) {
-  return launch_rotate<true>(gate_up, sign, M, K, x_i8, a_scale, stream);
+  return launch_rotate<true, false>(gate_up, sign, M, K, x_i8, a_scale, stream);
+}
+
+hipError_t launch_rotate_bf16(const uint16_t* x, const int8_t* sign, int64_t M, int64_t K,
+                              uint16_t* r, hipStream_t stream) {
+  return launch_rotate<false, true>(x, sign, M, K, reinterpret_cast<int8_t*>(r), nullptr, stream);
 }
 
 }  // namespace twl

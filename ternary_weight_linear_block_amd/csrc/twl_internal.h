@@ -16,6 +16,12 @@ struct DeviceInfo {
 
 hipError_t launch_rotate_quant(const uint16_t* x, const int8_t* sign, int64_t M, int64_t K,
                                int8_t* x_i8, float* a_scale, hipStream_t stream);
+// The rotation alone: r [M, K] as bf16 bit patterns.
+hipError_t launch_rotate_bf16(const uint16_t* x, const int8_t* sign, int64_t M, int64_t K,
+                              uint16_t* r, hipStream_t stream);
+// Exact-dequant bf16 reference linear: y = r_bf16 . (code * bf16(s))^T in fp32.
+hipError_t launch_reference_bf16(const uint16_t* r, const uint8_t* packed, const uint16_t* s,
+                                 int64_t M, int64_t N, int64_t K, float* y, hipStream_t stream);
 // gate_up: bf16 [M, 2K]; rotates bf16(SiLU(gate) * up).
 hipError_t launch_silu_mul_rotate_quant(const uint16_t* gate_up, const int8_t* sign, int64_t M,
                                         int64_t K, int8_t* x_i8, float* a_scale,

@@ -335,3 +335,24 @@ def test_silu_mul_rotate_edge_values(twl):
     assert np.array_equal(host(sc).view(np.uint32), osc.view(np.uint32))
     assert np.array_equal(host(xi), ox)
     assert osc[2] == 0
+
+
+# ------------------------------------------- bf16 reference path (R15)
+
+@pytest.mark.parametrize("M,N,K,rows", [(16, 256, 1024, None), (300, 513, 2048, None),
+                                        (1, 17408, 5120, None), (512, 17408, 5120, 48)])
+def test_reference_linear_bf16(twl, M, N, K, rows):
+    # the rotation alone is bit-exact; y within the fp32 accumulation bound of
+    # the exact sum (rows: check a sample of token rows of a large layer)
+    layer = W.make_layer(6000 + M + N, M, K, N)
+    announce(f"rotate_act_bf16 M={M} K={K}")
+    r = twl.rotate_act_bf16(dev(layer.x_bits.view(np.int16)), dev(layer.sign))
+    r_bits = host(r.view(torch.int16)).view(np.uint16)
+    assert np.array_equal(r_bits, O.rotate_bf16(layer.x_bits, layer.sign))
+    packed, _, _ = twl.pack_ternary(dev(layer.code), dev(layer.s_bits.view(np.int16)))
+    announce(f"reference_linear_bf16 M={M} N={N} K={K}")
+    y = host(twl.reference_linear_bf16(r, packed, dev(layer.s_bits.view(np.int16))))
+    sel = np.arange(M) if rows is None else np.random.default_rng(1).choice(M, rows, replace=False)
+    want, scale = O.reference_linear_bf16(r_bits[sel], layer.code, layer.s_bits)
+    err = np.abs(y[sel].astype(np.float64) - want)
+    assert np.all(err <= K * 2.0**-24 * scale + 1e-30), float(np.max(err / (scale + 1e-30)))
