@@ -132,9 +132,11 @@ struct QTables {
 };
 
 __device__ __forceinline__ QTables make_tables(int qv) {
-  const uint32_t neg = static_cast<uint32_t>(-qv) & 0xFFu;
-  const uint32_t pos = static_cast<uint32_t>(qv) & 0xFFu;
-  return QTables{neg | (pos << 8), pos, neg};
+  // ta = [-q, +q, 0, 0]; tb0 = q (only its byte 0 is ever selected);
+  // tb1 = [-q, 0, 0, 0] (byte 0, and the zero sign bit of byte 1)
+  const uint32_t q = static_cast<uint32_t>(qv);
+  const uint32_t neg = 0u - q;
+  return QTables{__builtin_amdgcn_perm(q, neg, 0x0C0C0400u), q, __builtin_amdgcn_perm(0u, neg, 0x0C0C0C00u)};
 }
 
 __device__ __forceinline__ v4i unpack16(uint32_t w, const QTables& t) {
@@ -492,54 +494,60 @@ __global__ __launch_bounds__(64 * 4 * WK, 1) void gemm_kernel(GemmArgs p) {
   wait_vmcnt<(S - 1) * T::LOADS_PER_STAGE>();  // own loads of the first stage done
   bare_barrier();
   v4i a0[RM][KH], a1[RM][KH];
-  words_t bw[RN];
-  int qb[RN];
+  // The stage loop is unrolled by U (a multiple of S and of 2), so that the
+  // buffer of every stage is a compile-time constant (LDS addresses fold into
+  // the instructions' offsets) and the packed words alternate between two
+  // register sets instead of being copied.
+  constexpr int U = S % 2 == 0 ? S : 2 * S;
+  words_t bwv[2][RN];
+  int qbv[2][RN];
   read_a(0, 0, a0);
-  read_b(0, st_begin, bw, qb);
-  int buf = 0;
-  for (int st = st_begin; st < st_end; ++st) {
-    const int nbuf = buf == S - 1 ? 0 : buf + 1;
-    const int dst = min(st + S, st_end - 1);  // stage whose DMA reuses this buffer
-    QTables tab[RN];
+  read_b(0, st_begin, bwv[0], qbv[0]);
+  for (int st0 = st_begin; st0 < st_end; st0 += U) {
 #pragma unroll
-    for (int j = 0; j < RN; ++j) tab[j] = make_tables(qb[j]);
-    read_a(buf, 1, a1);
-    __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the first half's MFMAs
-    // first half
+    for (int u = 0; u < U; ++u) {
+      const int st = st0 + u;
+      if (st >= st_end) break;
+      const int buf = u % S, nbuf = (u + 1) % S;
+      const int cur = u & 1, nxt = cur ^ 1;
+      const int dst = min(st + S, st_end - 1);  // stage whose DMA reuses this buffer
+      QTables tab[RN];
 #pragma unroll
-    for (int t = 0; t < KH; ++t)
+      for (int j = 0; j < RN; ++j) tab[j] = make_tables(qbv[cur][j]);
+      read_a(buf, 1, a1);
+      __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the first half's MFMAs
+      // first half
 #pragma unroll
-      for (int j = 0; j < RN; ++j) {
-        const v4i b = unpack16(bw[j][t], tab[j]);
+      for (int t = 0; t < KH; ++t)
 #pragma unroll
-        for (int i = 0; i < RM; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[i][t], b, acc[i][j], 0, 0, 0);
+        for (int j = 0; j < RN; ++j) {
+          const v4i b = unpack16(bwv[cur][j][t], tab[j]);
+#pragma unroll
+          for (int i = 0; i < RM; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[i][t], b, acc[i][j], 0, 0, 0);
+        }
+      if (st + 1 < st_end) {
+        wait_lgkm0();  // this wave's reads of buffer `buf` have landed
+        wait_vmcnt<(S - 2) * T::LOADS_PER_STAGE>();  // own loads of stage st+1 done
+        bare_barrier();  // everyone's stage st+1 is in LDS; everyone is past buffer `buf`
+        read_a(nbuf, 0, a0);
+        read_b(nbuf, st + 1, bwv[nxt], qbv[nxt]);
+        __builtin_amdgcn_sched_barrier(0);  // and these ahead of the second half's
       }
-    words_t bw1[RN];  // the second half's words: bw is refilled with the next stage below
+      // second half, with this stage's DMA into the freed buffer
 #pragma unroll
-    for (int j = 0; j < RN; ++j) bw1[j] = bw[j];
-    if (st + 1 < st_end) {
-      wait_lgkm0();  // this wave's reads of buffer `buf` have landed
-      wait_vmcnt<(S - 2) * T::LOADS_PER_STAGE>();  // own loads of stage st+1 done
-      bare_barrier();  // everyone's stage st+1 is in LDS; everyone is past buffer `buf`
-      read_a(nbuf, 0, a0);
-      read_b(nbuf, st + 1, bw, qb);
-      __builtin_amdgcn_sched_barrier(0);  // and these ahead of the second half's
+      for (int t = 0; t < KH; ++t)
+#pragma unroll
+        for (int j = 0; j < RN; ++j) {
+          const v4i b = unpack16(bwv[cur][j][KH + t], tab[j]);
+#pragma unroll
+          for (int i = 0; i < RM; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[i][t], b, acc[i][j], 0, 0, 0);
+#pragma unroll
+          for (int k = 0; k < T::LOADS_PER_STAGE; ++k)
+            if ((k * SLOTS) / T::LOADS_PER_STAGE == t * RN + j) issue_one(k, dst, buf);
+        }
     }
-    // second half, with this stage's DMA into the freed buffer
-#pragma unroll
-    for (int t = 0; t < KH; ++t)
-#pragma unroll
-      for (int j = 0; j < RN; ++j) {
-        const v4i b = unpack16(bw1[j][KH + t], tab[j]);
-#pragma unroll
-        for (int i = 0; i < RM; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[i][t], b, acc[i][j], 0, 0, 0);
-#pragma unroll
-        for (int k = 0; k < T::LOADS_PER_STAGE; ++k)
-          if ((k * SLOTS) / T::LOADS_PER_STAGE == t * RN + j) issue_one(k, dst, buf);
-      }
-    buf = nbuf;
   }
   wait_vmcnt<0>();  // drain the padding loads of the tail before the LDS is reused
 

@@ -6,8 +6,8 @@ around inline asm, so the kernel is only correct while the compiler never uses
 M0 for anything else.  This test compiles the GEMM to assembly with the
 library's own flags and checks that every M0 write is one of ours (an
 s_mov_b32 from an SGPR followed by a global_load_lds) and that M0 is read by
-nothing else.  It also checks the main loop keeps a single vmcnt wait and no
-accumulator copies.
+nothing else.  It also checks the main loop keeps a single vmcnt wait per
+pipeline stage and no accumulator copies.
 """
 import os
 import re
@@ -85,11 +85,16 @@ def _loops(body):
     return {k: "\n".join(v) for k, v in loops.items()}
 
 
-def test_main_loop_has_one_wait_and_no_accumulator_copies(asm):
+def test_main_loop_has_one_wait_per_stage_and_no_accumulator_copies(asm):
+    # the stage loop is unrolled by a whole number of pipeline stages: one
+    # vmcnt wait per stage (RM x ceil(FN/2) x 4/WK MFMAs), no AGPR copies
     for name, body in _kernels(asm).items():
+        rm, fn, wk = (int(v) for v in re.search(r"gemm_kernelILi(\d+)ELi(\d+)ELi(\d+)E", name).groups())
         mains = [t for t in _loops(body).values() if "v_mfma" in t]
         assert len(mains) == 1, (name, len(mains))
         loop = mains[0]
-        assert loop.count("vmcnt") == 1, name
+        n_mfma = loop.count("v_mfma_i32_32x32x32_i8")
+        per_stage = rm * ((fn + 1) // 2) * (4 // wk)
+        assert n_mfma > 0 and n_mfma % per_stage == 0, (name, n_mfma)
+        assert loop.count("vmcnt") == n_mfma // per_stage, name
         assert "v_accvgpr" not in loop, name
-        assert "v_mfma_i32_32x32x32_i8" in loop, name
