@@ -173,9 +173,6 @@ struct Tile {
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int LOADS_PER_STAGE = A_PER_WAVE + B_PER_WAVE;
   static constexpr int SLOT_INTS = 4 * RM * RN * 64 * 16;  // one split's partial tile
-  // wave-pair reduction: fragments exchanged per round through the LDS
-  static constexpr int XCH_FRAGS = LDS_BYTES / (4 * 4096);
-  static_assert(WK == 1 || XCH_FRAGS >= 1, "LDS too small for the wave-pair exchange");
   static_assert((STAGES - 1) * LOADS_PER_STAGE < 64, "vmcnt range");
 };
 
@@ -223,11 +220,13 @@ __device__ __forceinline__ void lds_wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Only the fragments i * RN + j in [f_lo, f_hi) are written (the wave pair
+// splits the tile's fragments between its two waves).
 template <int RM, int FN, int OUT>
 __device__ __forceinline__ void store_tile(const v16i (&acc)[RM][(FN + 1) / 2], void* out,
                                            const float* row_scale, const float* col_scale,
                                            int M, int N, int m0, int n0, int wm, int wn,
-                                           int lane, int32_t* tr) {
+                                           int lane, int32_t* tr, int f_lo, int f_hi) {
   constexpr int RN = (FN + 1) / 2;
   const int l32 = lane & 31, half = lane >> 5;
   const bool vec = (N & 3) == 0;
@@ -241,6 +240,7 @@ __device__ __forceinline__ void store_tile(const v16i (&acc)[RM][(FN + 1) / 2], 
     const float cscale = OUT == kOutAcc ? 0.0f : col_scale[cl] * (1.0f / 127.0f);
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
+      if (i * RN + j < f_lo || i * RN + j >= f_hi) continue;
       const int rbase = wm * 32 * RM + 32 * i;  // first row of the fragment in the tile
       if (!vec) {
 #pragma unroll
@@ -335,9 +335,6 @@ __global__ __launch_bounds__(64 * 4 * WK, 1) void gemm_kernel(GemmArgs p) {
   // output stores would order every load behind the stores before it)
   __shared__ __attribute__((aligned(16))) float row_scale[T::BM];
   __shared__ __attribute__((aligned(16))) float col_scale[(T::BN + 63) / 64 * 64];
-  // output transposes of the four storing waves
-  __shared__ __attribute__((aligned(16))) int32_t tr_lds[4][32 * kTrStride];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -551,61 +548,93 @@ __global__ __launch_bounds__(64 * 4 * WK, 1) void gemm_kernel(GemmArgs p) {
   }
   wait_vmcnt<0>();  // drain the padding loads of the tail before the LDS is reused
 
-  // ---- add the wave pair's partials: wk = 1 hands its accumulators to wk = 0
-  // through the (now idle) pipeline buffers, T::XCH_FRAGS fragments per round.
+  // ---- add the wave pair's partials.  The pair splits the fragments: wk = 0
+  // keeps f = i * RN + j in [0, H), wk = 1 keeps [H, NF); each wave hands the
+  // other half to its partner through the (now idle) pipeline buffers, XR
+  // fragments per wave per round, and both then store their own half.
+  constexpr int NF = RM * RN;
+  constexpr int H = WK == 2 ? (NF + 1) / 2 : NF;
   if (WK == 2) {
-    constexpr int NF = RM * RN;
+    constexpr int XR = T::LDS_BYTES / (8 * 4096);
+    static_assert(XR >= 1, "LDS too small for the wave-pair exchange");
     int32_t* xch = reinterpret_cast<int32_t*>(smem);
     const int pair = wave & 3;
+    // slot of the k-th fragment sent in a round by wave (pair, sender wk)
+    const auto slot = [&](int k, int sender, int c) {
+      return xch + ((((k * 2 + sender) * 4 + pair) * 4 + c) * 64 + lane) * 4;
+    };
 #pragma unroll
-    for (int f0 = 0; f0 < NF; f0 += T::XCH_FRAGS) {
+    for (int r0 = 0; r0 < H; r0 += XR) {
       bare_barrier();  // the buffers are free (stage reads / previous round done)
-      if (wk == 1) {
 #pragma unroll
-        for (int f = f0; f < f0 + T::XCH_FRAGS && f < NF; ++f)
+      for (int k = 0; k < XR; ++k) {
+        const int fs0 = H + r0 + k, fs1 = r0 + k;  // what wk = 0 / wk = 1 sends
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const v16i& a = acc[f / RN][f % RN];
-            const v4i v = {a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]};
-            *reinterpret_cast<v4i*>(xch + ((((f - f0) * 4 + pair) * 4 + c) * 64 + lane) * 4) = v;
+        for (int c = 0; c < 4; ++c) {
+          if (wk == 0 && fs0 < NF) {
+            const v16i& a = acc[fs0 / RN][fs0 % RN];
+            *reinterpret_cast<v4i*>(slot(k, 0, c)) = v4i{a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]};
           }
+          if (wk == 1 && fs1 < H) {
+            const v16i& a = acc[fs1 / RN][fs1 % RN];
+            *reinterpret_cast<v4i*>(slot(k, 1, c)) = v4i{a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]};
+          }
+        }
       }
       __syncthreads();
-      if (wk == 0) {
 #pragma unroll
-        for (int f = f0; f < f0 + T::XCH_FRAGS && f < NF; ++f)
+      for (int k = 0; k < XR; ++k) {
+        const int fr0 = r0 + k, fr1 = H + r0 + k;  // what wk = 0 / wk = 1 receives
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const v4i v = *reinterpret_cast<const v4i*>(xch + ((((f - f0) * 4 + pair) * 4 + c) * 64 + lane) * 4);
-            v16i& a = acc[f / RN][f % RN];
+        for (int c = 0; c < 4; ++c) {
+          if (wk == 0 && fr0 < H) {
+            const v4i v = *reinterpret_cast<const v4i*>(slot(k, 1, c));
+            v16i& a = acc[fr0 / RN][fr0 % RN];
             a[4 * c] += v.x;
             a[4 * c + 1] += v.y;
             a[4 * c + 2] += v.z;
             a[4 * c + 3] += v.w;
           }
+          if (wk == 1 && fr1 < NF) {
+            const v4i v = *reinterpret_cast<const v4i*>(slot(k, 0, c));
+            v16i& a = acc[fr1 / RN][fr1 % RN];
+            a[4 * c] += v.x;
+            a[4 * c + 1] += v.y;
+            a[4 * c + 2] += v.z;
+            a[4 * c + 3] += v.w;
+          }
+        }
       }
     }
+    __syncthreads();  // every wave is past the exchange buffers before they become transposes
+  } else {
+    __syncthreads();  // every wave is past its last stage before the buffers become transposes
   }
-  if (wk != 0) return;
+  const int f_lo = wk == 0 ? 0 : H, f_hi = wk == 0 ? H : NF;
 
   if (p.splits > 1) {
     // split-K: store this split's exact partial tile; splitk_reduce_kernel adds
     // the splits and runs the epilogue.  Slot layout: fragment, 16-byte chunk,
     // lane (each store instruction writes 1 KB contiguous).
     int32_t* mine = p.ws_part + (static_cast<size_t>(w.tile) * p.splits + w.split) * T::SLOT_INTS;
+    const int pair = wave & 3;
 #pragma unroll
     for (int i = 0; i < RM; ++i)
 #pragma unroll
-      for (int j = 0; j < RN; ++j)
+      for (int j = 0; j < RN; ++j) {
+        if (i * RN + j < f_lo || i * RN + j >= f_hi) continue;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const v4i v = {acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
-          *reinterpret_cast<v4i*>(mine + ((((wave * RM + i) * RN + j) * 4 + c) * 64 + lane) * 4) = v;
+          *reinterpret_cast<v4i*>(mine + ((((pair * RM + i) * RN + j) * 4 + c) * 64 + lane) * 4) = v;
         }
+      }
     return;
   }
+  // each wave transposes its fragments in its own 5 KB of the idle pipeline buffers
+  static_assert(T::LDS_BYTES >= 8 * 32 * kTrStride * 4, "LDS too small for the output transposes");
   store_tile<RM, FN, OUT>(acc, p.out, row_scale, col_scale, M, N, m0, n0, wm, wn, lane,
-                          tr_lds[wave & 3]);
+                          reinterpret_cast<int32_t*>(smem) + wave * 32 * kTrStride, f_lo, f_hi);
 }
 
 // Split-K second pass: one workgroup per block tile, four waves in the same
@@ -649,7 +678,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
   }
   __syncthreads();
   store_tile<RM, FN, OUT>(acc, p.out, row_scale, col_scale, p.M, p.N, m0, n0, wave & 1,
-                          wave >> 1, lane, tr_lds[wave]);
+                          wave >> 1, lane, tr_lds[wave], 0, RM * RN);
 }
 
 // ---------------------------------------------------------------- planner
