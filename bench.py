@@ -6,8 +6,12 @@
 Headline (the JSON `value`): one prefill step of the gate/up projection,
 M=512 tokens, K=5120, N=17408 -- rotate_quant_act followed by ternary_linear
 (int8-MFMA GEMM with fused 2-bit unpack and rescale) -- reported as int8 TOPS
-(2*M*N*K per step / step time).  Packing is a load-time operation and is done
-once before timing.  Inputs are seeded synthetic data with the pages' layer
+(2*M*N*K per step / step time), the steps launched one by one from Python.
+The same steps captured once as a HIP graph and replayed (the launch path of
+a serving loop) are reported beside it ("ms_per_step_graph"): slower for this
+prefill step, much faster for the small decode steps, where host launch
+overhead dominates.  Packing is a load-time operation and is done once before
+timing.  Inputs are seeded synthetic data with the pages' layer
 shapes; weights cycle through enough copies (>= 1.1 GB) that every step reads
 them from HBM rather than from the 256 MB last-level cache.
 
@@ -108,8 +112,9 @@ def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, kernel_iters=50, b
     """warmup + timed steps of rotate_quant_act + ternary_linear.
 
     Returns (ms per step from the wall clock around exactly `steps` eager
-    steps, mean ms of one rotate_quant_act launch, mean ms of one
-    ternary_linear call); the per-kernel means come from HIP events around a
+    steps, the same for the `steps` steps launched as one captured HIP graph,
+    mean ms of one rotate_quant_act launch, mean ms of one ternary_linear call);
+    the per-kernel means come from HIP events around a
     captured graph of `kernel_iters` back-to-back launches of that kernel alone
     (weights cycled), see graph_time_ms.  With bf16=True a fourth value is
     the mean ms of one ternary_linear call that writes y in bf16 instead.
@@ -140,6 +145,25 @@ def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, kernel_iters=50, b
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / steps
 
+    # the same `steps` steps (weights still cycled) captured once as a HIP
+    # graph, the way a serving loop launches them; one untimed replay, then
+    # one replay timed between two synchronizations
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(steps):
+            rotq()
+            linear(i)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    ms_graph = (time.perf_counter() - t0) * 1e3 / steps
+    del g
+
     rq = graph_time_ms(torch, rotq, kernel_iters)
     ctr = [0]
 
@@ -149,7 +173,7 @@ def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, kernel_iters=50, b
 
     lin = graph_time_ms(torch, linear_next, kernel_iters)
     if not bf16:
-        return ms_step, rq, lin
+        return ms_step, ms_graph, rq, lin
     y16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
 
     def linear_bf16_next():
@@ -158,7 +182,7 @@ def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, kernel_iters=50, b
         ctr[0] += 1
 
     lin16 = graph_time_ms(torch, linear_bf16_next, kernel_iters)
-    return ms_step, rq, lin, lin16
+    return ms_step, ms_graph, rq, lin, lin16
 
 
 def traffic_for(kernel_src: str, workload: str):
@@ -222,7 +246,7 @@ def section_layer(torch, twl, name, steps, warmup):
     import workloads as W
     layer = W.make_config(name)
     x, sign, sets = upload_layer(torch, twl, layer, n_copies(layer.N, layer.K))
-    ms, rq, lin, lin16 = run_layer_steps(torch, twl, x, sign, sets, steps, warmup, bf16=True)
+    ms, ms_graph, rq, lin, lin16 = run_layer_steps(torch, twl, x, sign, sets, steps, warmup, bf16=True)
     ops = 2.0 * layer.M * layer.N * layer.K
     extra = {}
     if name == "prefill_gate_up":
@@ -250,7 +274,8 @@ def section_layer(torch, twl, name, steps, warmup):
         extra = {"silu_rotq_ms": round(fused, 5), "silu_rotq_gbs": round(fb / fused / 1e6, 1)}
         del gu
     out = {"M": layer.M, "K": layer.K, "N": layer.N, "ms_per_step": round(ms, 5),
-           "step_tops": round(ops / ms / 1e9, 2), "linear_ms": round(lin, 5),
+           "step_tops": round(ops / ms / 1e9, 2), "ms_per_step_graph": round(ms_graph, 5),
+           "step_tops_graph": round(ops / ms_graph / 1e9, 2), "linear_ms": round(lin, 5),
            "linear_tops": round(ops / lin / 1e9, 2),
            "linear_bf16_y_ms": round(lin16, 5), "linear_bf16_y_tops": round(ops / lin16 / 1e9, 2),
            "rotq_ms": round(rq, 5),
@@ -270,10 +295,11 @@ def section_decode(torch, twl, steps, warmup):
         per_m = {}
         for M in W.DECODE_MS:
             x = x_full[:M].contiguous()
-            ms, rq, lin = run_layer_steps(torch, twl, x, sign, sets, steps, warmup)
+            ms, ms_graph, rq, lin = run_layer_steps(torch, twl, x, sign, sets, steps, warmup)
             wb = weight_bytes(layer.N, layer.K)
             tot = wb + M * layer.K + M * 4 + 4 * M * layer.N
-            per_m[str(M)] = {"ms_per_step": round(ms, 5), "linear_ms": round(lin, 5),
+            per_m[str(M)] = {"ms_per_step": round(ms, 5), "ms_per_step_graph": round(ms_graph, 5),
+                             "linear_ms": round(lin, 5),
                              "weight_gbs": round(wb / lin / 1e6, 1),
                              "hbm_frac": round(wb / lin / 1e6 / PEAK_HBM_GBS, 4),
                              "total_gbs": round(tot / lin / 1e6, 1),
@@ -396,7 +422,9 @@ def main(argv=None) -> int:
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
            "data": "synthetic",
            "config": {"workload": "prefill_gate_up", "M": layer.M, "K": layer.K, "N": layer.N,
-                      "step": "rotate_quant_act + ternary_linear", "parallelism": "none (1 GPU)"},
+                      "step": "rotate_quant_act + ternary_linear",
+                      "launch": "eager (graph-launched figure in detail)",
+                      "parallelism": "none (1 GPU)"},
            "roofline": roofline, "cpu_baseline": cpu, "detail": detail}
     print(json.dumps(rec), flush=True)
     return 0
