@@ -356,3 +356,51 @@ def test_reference_linear_bf16(twl, M, N, K, rows):
     want, scale = O.reference_linear_bf16(r_bits[sel], layer.code, layer.s_bits)
     err = np.abs(y[sel].astype(np.float64) - want)
     assert np.all(err <= K * 2.0**-24 * scale + 1e-30), float(np.max(err / (scale + 1e-30)))
+
+
+# ------------------------------------------------------ HIP graph replays
+
+@pytest.mark.parametrize("M,N,K", [(512, 1000, 5120),    # GEMM
+                                   (40, 300, 32768),     # GEMM with split-K partials
+                                   (9, 200, 20480),      # MFMA decode, K slices + reduce
+                                   (5, 24575, 1024),     # row-balanced MFMA decode
+                                   (2, 1000, 5120)])     # dot4 decode
+def test_graph_replays_match_eager(twl, M, N, K):
+    # the path (rotation + linear) captured once in a graph; every replay,
+    # with eager work on the same buffers in between, must give the eager
+    # result bit for bit (the library records no memset and allocates nothing)
+    layer = W.make_layer(7000 + M + N, M, K, N)
+    x, sign = dev(layer.x_bits.view(np.int16)), dev(layer.sign)
+    packed, q, smax = twl.pack_ternary(dev(layer.code), dev(layer.s_bits.view(np.int16)))
+    x_i8 = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    a_scale = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = torch.full((max(1, twl.workspace_bytes(M, N, K)),), 0x5A, dtype=torch.uint8, device="cuda")
+
+    def step():
+        twl.rotate_quant_act(x, sign, out=(x_i8, a_scale))
+        twl.ternary_linear(x_i8, a_scale, packed, q, smax, out=y, workspace=ws)
+
+    announce(f"graph capture M={M} N={N} K={K}")
+    step()
+    want_y, want_x = host(y).copy(), host(x_i8).copy()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step()
+    for rep in range(4):
+        y.fill_(float("nan"))
+        x_i8.zero_()
+        announce(f"graph replay {rep} M={M} N={N} K={K}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(x_i8), want_x), f"replay {rep}: x_i8"
+        assert np.array_equal(host(y).view(np.uint32), want_y.view(np.uint32)), f"replay {rep}: y"
+        # eager work on the same workspace between replays
+        twl.ternary_linear_acc(x_i8, packed, q, workspace=ws)
+        torch.cuda.synchronize()
+    oy = O.ternary_linear(*O.rotate_quant_act(layer.x_bits, layer.sign), layer.code,
+                          *O.decompose_scales(layer.s_bits))
+    np.testing.assert_allclose(want_y, oy, rtol=Y_RTOL, atol=0)
