@@ -108,6 +108,48 @@ def graph_time_ms(torch, fn, iters: int, replays: int = 3) -> float:
     return best
 
 
+def event_time_ms(torch, fn, iters: int = 10, warm: int = 3) -> float:
+    """Mean ms of fn() over `iters` back-to-back calls, HIP events on the
+    current stream (for library calls that are not captured in a graph)."""
+    for _ in range(warm):
+        fn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def pages_int8_path(torch, twl, layer, x, sign, packed_q_smax):
+    """The pages' int8 design ([P1] section 4) on the same GPU, as an A/B point:
+    expand W_int8 = code * q in HBM every step (plain torch ops), the library
+    int8 GEMM (torch._int_mm, hipBLASLt on ROCm; B as a column-major view of
+    W_int8), and the per-token / per-row rescale as a torch elementwise pass."""
+    import numpy as np
+    _, q, smax = packed_q_smax
+    code = torch.from_numpy(np.ascontiguousarray(layer.code)).cuda()
+    x_i8, a_scale = twl.rotate_quant_act(x, sign)
+    q_rep = q.repeat_interleave(128, dim=1)
+    expand = lambda: code * q_rep
+    w = expand()
+    mm = lambda: torch._int_mm(x_i8, w.t())
+    acc = mm()
+    col = smax * (1.0 / 127.0)
+    rescale = lambda: acc.float() * a_scale[:, None] * col[None, :]
+    out = {"expand_ms": event_time_ms(torch, expand), "int_mm_ms": event_time_ms(torch, mm),
+           "rescale_ms": event_time_ms(torch, rescale)}
+    out["total_ms"] = out["expand_ms"] + out["int_mm_ms"] + out["rescale_ms"]
+    ops = 2.0 * layer.M * layer.N * layer.K
+    out["int_mm_tops"] = round(ops / out["int_mm_ms"] / 1e9, 2)
+    out = {k: (round(v, 5) if k.endswith("_ms") else v) for k, v in out.items()}
+    del code, q_rep, w, acc
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, kernel_iters=50, bf16=False):
     """warmup + timed steps of rotate_quant_act + ternary_linear.
 
@@ -262,6 +304,7 @@ def section_layer(torch, twl, name, steps, warmup):
         extra = {"reference_bf16_rotate_ms": round(rot_ms, 5), "reference_bf16_linear_ms": round(ref_ms, 5),
                  "reference_bf16_tflops": round(ops / ref_ms / 1e9, 2)}
         del r, yr, s_d
+        extra["pages_int8_path"] = pages_int8_path(torch, twl, layer, x, sign, sets[0])
     if layer.act == "silu_gate":
         # the fused SiLU(gate) * up + rotation of this layer's input, from a
         # [M, 2K] gate/up tensor (random bf16, drawn on the GPU)
