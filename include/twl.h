@@ -53,7 +53,7 @@ typedef enum {
 #define TWL_HBLOCK 1024      /* Hadamard block width along K              */
 #define TWL_GROUP 128        /* K elements per weight scale group         */
 #define TWL_MAX_K 65536      /* 64 blocks; |acc| <= 127*127*K < 2^31       */
-#define TWL_GEMV_MAX_M 24    /* decode batches up to this size use the GEMV */
+#define TWL_GEMV_MAX_M 24    /* decode batches up to this size use a decode kernel */
 
 /* Which kernel family computes the linear layer (twl_ternary_linear_ex). */
 typedef enum {
@@ -143,11 +143,12 @@ size_t twl_packed_bytes(int64_t N, int64_t K);
 size_t twl_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
- * ternary_linear -- [P1] section 4 (prefill GEMM) and section 5 (decode GEMV).
+ * ternary_linear -- [P1] section 4 (prefill GEMM) and section 5 (decode).
  *   acc[t,n] = sum_k x_i8[t,k] * code[n,k] * q[n, k/128]      (exact int32)
  *   y[t,n]   = acc[t,n] * a_scale[t] * smax[n] / 127           (fp32)
  *   Prefill sizes run an int8-MFMA GEMM that unpacks the 2-bit codes on chip;
- *   decode batches (M <= TWL_GEMV_MAX_M) run a packed-2-bit GEMV.  Both give
+ *   decode batches (M <= TWL_GEMV_MAX_M) stream the packed weights through a
+ *   dot4 GEMV (M < 4) or a 32-token-padded int8 MFMA kernel.  All give
  *   bit-identical acc.
  *   x_i8 [M,K], a_scale [M], packed (twl_packed_bytes(N,K) bytes), q [N,K/128],
  *   smax [N] as produced by the two calls above; y out: fp32 [M, N].

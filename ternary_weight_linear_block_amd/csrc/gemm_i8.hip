@@ -26,10 +26,12 @@
 //     BN = 32 FN columns split 2 along M x 2 along N; wave (wm, wn) owns RM row
 //     fragments and ceil(FN/2) column fragments (an odd FN leaves wn=1 one
 //     padding fragment), and the two waves (wk = 0, 1) of each (wm, wn) take
-//     k-steps {0,1} and {2,3} of every stage.  The pair's int32 partials are
-//     added through LDS at the end (exact).  Two waves per SIMD let one wave's
-//     unpack VALU and LDS reads run while the other's MFMAs execute; with one
-//     wave per SIMD these costs were measured to add up.
+//     k-steps {0,1} and {2,3} of every stage.  At the end the pair splits the
+//     tile's fragments in half and each wave adds its partner's int32
+//     partials for its half through LDS (exact), so all 8 waves store.  Two
+//     waves per SIMD let one wave's unpack VALU and LDS reads run while the
+//     other's MFMAs execute; with one wave per SIMD these costs were measured
+//     to add up.
 //   * Multi-stage pipeline (4 stages; 3 for 256-row tiles) of direct
 //     global->LDS loads (global_load_lds dwordx4: no VGPR staging).  A stage
 //     holds BM x 128 bytes of x_i8 (8 lanes per row; 16-byte chunks
@@ -49,6 +51,12 @@
 //     this multi-XCD part each fence writes back the L2.)
 //   * Tiles are ordered so that the workgroups sharing a column block (the
 //     same weights) land on the same XCD and its L2.
+//   * The stage loop is unrolled by the pipeline depth, so buffer offsets are
+//     constants and the packed words alternate between two register sets.
+//   * Output: each 32x32 fragment is transposed through a per-wave LDS scratch
+//     so that every lane writes 16 contiguous bytes (fp32 / int32 y: 4
+//     columns; bf16 y: 8 columns): the output phase is bound by the number of
+//     store transactions, not by bytes.
 #include "twl_internal.h"
 
 #include <algorithm>
