@@ -394,11 +394,28 @@ def section_stack(torch, twl, steps, warmup):
             step()
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / steps
+        # the same step captured once as a HIP graph (384 launches) and replayed
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms_graph = (time.perf_counter() - t0) * 1e3 / steps
+        del g
         ops = 2.0 * M * sum(N * K for _, K, N, _, _ in W.STACK_LINEARS) * W.N_LAYERS
         wb = sum(weight_bytes(N, K) for _, K, N, _, _ in W.STACK_LINEARS) * W.N_LAYERS
         out["prefill_M512" if M == 512 else "decode_M24"] = {
             "ms_per_step": round(ms, 4), "tops": round(ops / ms / 1e9, 2),
-            "weight_gbs": round(wb / ms / 1e6, 1), "launches": 6 * W.N_LAYERS}
+            "weight_gbs": round(wb / ms / 1e6, 1), "ms_per_step_graph": round(ms_graph, 4),
+            "tops_graph": round(ops / ms_graph / 1e9, 2), "weight_gbs_graph": round(wb / ms_graph / 1e6, 1),
+            "launches": 6 * W.N_LAYERS}
         del xs, bufs
     del layers
     torch.cuda.empty_cache()
