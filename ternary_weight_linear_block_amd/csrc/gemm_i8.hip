@@ -68,6 +68,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kStages = 4;       // pipeline depth
 constexpr int kStageK = 128;     // k per stage = one scale group
@@ -159,15 +160,15 @@ __device__ __forceinline__ v4i unpack16(uint32_t w, const QTables& t) {
 
 constexpr int kQTileBytes = 16384;  // q of a block tile: BN columns x its groups
 
-// Block tile of RM x FN fragments pairs (BM = 64 RM rows, BN = 32 FN columns)
-// computed by 4 WK waves: (wm, wn) split the tile 2 x 2 and, with WK = 2, a
-// pair of waves splits each stage's four k-steps.
-template <int RM, int FN, int WK>
+// Block tile of 2 RM x FN fragments (BM = 64 RM rows, BN = 32 FN columns)
+// computed by 2 WN WK waves: (wm, wn) split the tile 2 x WN and, with WK = 2,
+// a pair of waves splits each stage's four k-steps.
+template <int RM, int FN, int WK, int WN = 2>
 struct Tile {
-  static constexpr int RN = (FN + 1) / 2;      // column fragments per wave
+  static constexpr int RN = (FN + WN - 1) / WN;  // column fragments per wave
   static constexpr int BM = 64 * RM;
   static constexpr int BN = 32 * FN;
-  static constexpr int NW = 4 * WK;            // waves per workgroup
+  static constexpr int NW = 2 * WN * WK;       // waves per workgroup
   static constexpr int THREADS = 64 * NW;
   static constexpr int KS = 4 / WK;            // k-steps of a stage per wave
   static constexpr int STAGES = RM >= 4 ? 3 : kStages;
@@ -180,7 +181,7 @@ struct Tile {
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int LOADS_PER_STAGE = A_PER_WAVE + B_PER_WAVE;
-  static constexpr int SLOT_INTS = 4 * RM * RN * 64 * 16;  // one split's partial tile
+  static constexpr int SLOT_INTS = 2 * WN * RM * RN * 64 * 16;  // one split's partial tile
   static_assert((STAGES - 1) * LOADS_PER_STAGE < 64, "vmcnt range");
 };
 
@@ -194,6 +195,8 @@ struct GemmArgs {
   int32_t* ws_part;    // [tiles][splits][SLOT_INTS] split-K partial tiles
   int M, N, K;
   int tiles_m, tiles_n, splits, stages_per_split;
+  int tile_sn;         // column stride between block tiles (<= BN; a tile
+                       // computes BN columns and stores the first tile_sn)
 };
 
 // Writes one wave's RM x RN fragments of the output tile: fp32 y with the
@@ -319,7 +322,7 @@ struct WorkItem {
 };
 
 __device__ __forceinline__ WorkItem work_item(int bid, int tiles_m, int tiles_n, int splits,
-                                              int bm, int bn) {
+                                              int bm, int sn) {
   const int total = tiles_m * tiles_n * splits;
   const int per = total / kXcds, rem = total % kXcds;
   const int xcd = bid % kXcds;
@@ -328,13 +331,198 @@ __device__ __forceinline__ WorkItem work_item(int bid, int tiles_m, int tiles_n,
   w.split = lin % splits;
   w.tile = lin / splits;
   w.m0 = (w.tile % tiles_m) * bm;
-  w.n0 = (w.tile / tiles_m) * bn;
+  w.n0 = (w.tile / tiles_m) * sn;
   return w;
 }
 
-template <int RM, int FN, int WK, int OUT>
-__global__ __launch_bounds__(64 * 4 * WK, 1) void gemm_kernel(GemmArgs p) {
-  using T = Tile<RM, FN, WK>;
+// LDS-only workgroup barrier: this wave's LDS operations have completed, then
+// the waves meet (outstanding global stores are not waited for).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Register half of an accumulator fragment: in the 32x32 layout register r
+// holds row 8 (r / 4) + 4 half + (r % 4), so registers 0-7 are rows 0-15 and
+// registers 8-15 rows 16-31.
+__device__ __forceinline__ v8i reg_half(const v16i& a, bool upper) {
+  const v8i lo = __builtin_shufflevector(a, a, 0, 1, 2, 3, 4, 5, 6, 7);
+  const v8i hi = __builtin_shufflevector(a, a, 8, 9, 10, 11, 12, 13, 14, 15);
+  return upper ? hi : lo;
+}
+
+// Everything after the main loop for one wave.
+//
+// Wave-pair exchange (WK = 2): both waves of a pair hold int32 partials of the
+// same RM x RN fragments over complementary k-steps.  Wave wk keeps rows
+// [16 wk, 16 wk + 16) of every fragment (register half wk) and hands the
+// other half to its partner through the idle pipeline buffers, XR fragments
+// per round; the received half is added (exact).  wk only selects registers
+// and offsets, so the code has no per-fragment branches and each round is one
+// burst of LDS writes, a barrier and one burst of reads.
+//
+// Output: each kept half-fragment (16 rows x 32 columns) goes through a
+// per-wave LDS transpose (two buffers, alternated, so that one fragment is
+// written and read back while the stores of the previous one issue) and comes
+// back as 4 consecutive columns per lane (8 for bf16 when N % 8 == 0): one
+// 16-byte store covers 8 rows (bf16: 16).  Rows past M and columns past N are
+// not stored (per-store predicates); with N % 4 != 0 the values are stored one
+// by one straight from the registers.
+//
+// Split-K: the split's exact partial tile goes to the workspace instead, in
+// the layout splitk_reduce_kernel reads (fragment, 16-byte chunk, lane).
+template <int RM, int FN, int WK, int WN, int OUT>
+__device__ __forceinline__ void finish_tile(v16i (&acc)[RM][(FN + WN - 1) / WN], const GemmArgs& p,
+                                            const WorkItem& w, int8_t* smem, const float* row_scale,
+                                            const float* col_scale, int wave, int wk, int lane) {
+  using T = Tile<RM, FN, WK, WN>;
+  constexpr int RN = T::RN, NF = RM * RN, NP = 2 * WN;  // NP: (wm, wn) pairs
+  const int wm = wave & 1, wn = (wave >> 1) % WN, pair = wave % NP;
+  const bool upper = WK == 2 && wk == 1;
+  v8i kept[NF];
+#pragma unroll
+  for (int q = 0; q < NF; ++q) kept[q] = reg_half(acc[q / RN][q % RN], upper);
+  if (WK == 2) {
+    constexpr int XR = T::LDS_BYTES / (T::NW * 2 * 1024) < NF ? T::LDS_BYTES / (T::NW * 2 * 1024) : NF;
+    static_assert(XR >= 1, "LDS too small for the wave-pair exchange");
+    int32_t* xch = reinterpret_cast<int32_t*>(smem);
+    // 16-byte chunk c (0, 1) of fragment slot k sent by wave (pair, sender)
+    const auto slot = [&](int k, int sender, int c) {
+      return xch + ((((k * 2 + sender) * NP + pair) * 2 + c) * 64 + lane) * 4;
+    };
+#pragma unroll
+    for (int r0 = 0; r0 < NF; r0 += XR) {
+      bare_barrier();  // the buffers are free (stage reads / previous round done)
+#pragma unroll
+      for (int k = 0; k < XR && r0 + k < NF; ++k) {
+        const v8i s = reg_half(acc[(r0 + k) / RN][(r0 + k) % RN], !upper);
+        *reinterpret_cast<v4i*>(slot(k, wk, 0)) = __builtin_shufflevector(s, s, 0, 1, 2, 3);
+        *reinterpret_cast<v4i*>(slot(k, wk, 1)) = __builtin_shufflevector(s, s, 4, 5, 6, 7);
+      }
+      lds_barrier();
+#pragma unroll
+      for (int k = 0; k < XR && r0 + k < NF; ++k) {
+        const v4i i0 = *reinterpret_cast<const v4i*>(slot(k, wk ^ 1, 0));
+        const v4i i1 = *reinterpret_cast<const v4i*>(slot(k, wk ^ 1, 1));
+        kept[r0 + k] += __builtin_shufflevector(i0, i1, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    }
+  }
+  // every wave is past the exchange (or its last stage) before the buffers
+  // become transposes
+  lds_barrier();
+  const int l32 = lane & 31, half = lane >> 5;
+  const int row_off = upper ? 16 : 0;  // first fragment row this wave outputs
+  if (p.splits > 1) {
+    int32_t* mine = p.ws_part + (static_cast<size_t>(w.tile) * p.splits + w.split) * T::SLOT_INTS;
+#pragma unroll
+    for (int q = 0; q < NF; ++q) {
+      const int i = q / RN, j = q % RN;
+      const int c0 = WK == 2 ? 2 * wk : 0;
+      int32_t* dst = mine + ((((pair * RM + i) * RN + j) * 4 + c0) * 64 + lane) * 4;
+      *reinterpret_cast<v4i*>(dst) = __builtin_shufflevector(kept[q], kept[q], 0, 1, 2, 3);
+      *reinterpret_cast<v4i*>(dst + 256) = __builtin_shufflevector(kept[q], kept[q], 4, 5, 6, 7);
+      if (WK == 1) {
+        const v8i hi = reg_half(acc[i][j], true);
+        *reinterpret_cast<v4i*>(dst + 512) = __builtin_shufflevector(hi, hi, 0, 1, 2, 3);
+        *reinterpret_cast<v4i*>(dst + 768) = __builtin_shufflevector(hi, hi, 4, 5, 6, 7);
+      }
+    }
+    return;
+  }
+  static_assert(WK == 2, "the output path covers one register half per wave (wave pairs)");
+  const int M = p.M, N = p.N, m0 = w.m0, n0 = w.n0;
+  const int n_end = min(N, n0 + p.tile_sn);  // columns this tile stores
+  if ((N & 3) != 0) {
+    // rare shapes: element stores straight from the registers
+#pragma unroll
+    for (int q = 0; q < NF; ++q) {
+      const int f = wn * RN + q % RN;
+      const int col = n0 + 32 * f + l32;
+      if ((FN % WN != 0 && f >= FN) || col >= n_end) continue;
+      const float cscale = OUT == kOutAcc ? 0.0f : col_scale[32 * f + l32] * (1.0f / 127.0f);
+      const int rbase = wm * 32 * RM + 32 * (q / RN) + row_off;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int rl = rbase + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (m0 + rl < M)
+          store_out(p.out, static_cast<size_t>(m0 + rl) * N + col, OUT, kept[q][r],
+                    OUT == kOutAcc ? 0.0f : static_cast<float>(kept[q][r]) * row_scale[rl] * cscale);
+      }
+    }
+    return;
+  }
+  constexpr int kHalfWords = 16 * kTrStride;  // one transpose buffer
+  static_assert(T::LDS_BYTES >= T::NW * 2 * kHalfWords * 4, "LDS too small for the output transposes");
+  int32_t* tr0 = reinterpret_cast<int32_t*>(smem) + wave * 2 * kHalfWords;
+  const bool bf16x8 = OUT == kOutBf16 && (N & 7) == 0;
+  v4i rd[2][2];
+  // transpose kept half-fragment q through buffer b into rd[b]
+  const auto stage = [&](int q, int b) {
+    const int f = wn * RN + q % RN;
+    const int rbase = wm * 32 * RM + 32 * (q / RN) + row_off;
+    const float cscale = OUT == kOutAcc ? 0.0f : col_scale[32 * f + l32] * (1.0f / 127.0f);
+    int32_t* tr = tr0 + b * kHalfWords;
+    lds_wave_sync();  // earlier reads of this buffer stay ahead of these writes
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int rr = 8 * (r >> 2) + 4 * half + (r & 3);
+      tr[rr * kTrStride + l32] =
+          OUT == kOutAcc ? kept[q][r]
+                         : __float_as_int(static_cast<float>(kept[q][r]) * row_scale[rbase + rr] * cscale);
+    }
+    lds_wave_sync();
+    if (bf16x8) {
+      const int rr = lane >> 2, c8 = 8 * (lane & 3);
+      rd[b][0] = *reinterpret_cast<const v4i*>(tr + rr * kTrStride + c8);
+      rd[b][1] = *reinterpret_cast<const v4i*>(tr + rr * kTrStride + c8 + 4);
+    } else {
+      const int c4 = 4 * (lane & 7);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) rd[b][k] = *reinterpret_cast<const v4i*>(tr + (8 * k + (lane >> 3)) * kTrStride + c4);
+    }
+  };
+  const auto emit = [&](int q, int b) {
+    const int f = wn * RN + q % RN;
+    if (FN % WN != 0 && f >= FN) return;  // padding fragment (wave-uniform)
+    const int grow0 = m0 + wm * 32 * RM + 32 * (q / RN) + row_off;
+    if (bf16x8) {
+      const int grow = grow0 + (lane >> 2), gcol = n0 + 32 * f + 8 * (lane & 3);
+      if (grow < M && gcol < n_end)
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + static_cast<size_t>(grow) * N + gcol) =
+            make_uint4(bf16_pair(rd[b][0].x, rd[b][0].y), bf16_pair(rd[b][0].z, rd[b][0].w),
+                       bf16_pair(rd[b][1].x, rd[b][1].y), bf16_pair(rd[b][1].z, rd[b][1].w));
+      return;
+    }
+    const int gcol = n0 + 32 * f + 4 * (lane & 7);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int grow = grow0 + 8 * k + (lane >> 3);
+      if (grow < M && gcol < n_end) {  // n_end % 4 == 0: all four columns are in range
+        const size_t o = static_cast<size_t>(grow) * N + gcol;
+        if (OUT == kOutBf16)
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) =
+              make_uint2(bf16_pair(rd[b][k].x, rd[b][k].y), bf16_pair(rd[b][k].z, rd[b][k].w));
+        else
+          *reinterpret_cast<v4i*>(static_cast<int32_t*>(p.out) + o) = rd[b][k];
+      }
+    }
+  };
+  stage(0, 0);
+#pragma unroll
+  for (int q = 1; q < NF; ++q) {
+    __builtin_amdgcn_sched_barrier(0);
+    stage(q, q & 1);
+    emit(q - 1, (q - 1) & 1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  emit(NF - 1, (NF - 1) & 1);
+}
+
+template <int RM, int FN, int WK, int WN, int OUT>
+__global__ __launch_bounds__(64 * 2 * WN * WK, 1) void gemm_kernel(GemmArgs p) {
+  using T = Tile<RM, FN, WK, WN>;
   constexpr int RN = T::RN, BN = T::BN;
   __shared__ __attribute__((aligned(1024))) int8_t smem[T::LDS_BYTES];
   __shared__ __attribute__((aligned(16))) int8_t q_lds[kQTileBytes + 256];
@@ -347,12 +535,12 @@ __global__ __launch_bounds__(64 * 4 * WK, 1) void gemm_kernel(GemmArgs p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1;
-  const int wn = (wave >> 1) & 1;
-  const int wk = WK == 1 ? 0 : wave >> 2;  // which k-steps of each stage
+  const int wn = (wave >> 1) % WN;
+  const int wk = WK == 1 ? 0 : wave / (2 * WN);  // which k-steps of each stage
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  const WorkItem w = work_item(blockIdx.x, p.tiles_m, p.tiles_n, p.splits, T::BM, BN);
+  const WorkItem w = work_item(blockIdx.x, p.tiles_m, p.tiles_n, p.splits, T::BM, p.tile_sn);
   const int m0 = w.m0, n0 = w.n0;
   const int M = p.M, N = p.N, K = p.K;
   const int G = K >> 7;
@@ -555,94 +743,7 @@ __global__ __launch_bounds__(64 * 4 * WK, 1) void gemm_kernel(GemmArgs p) {
     }
   }
   wait_vmcnt<0>();  // drain the padding loads of the tail before the LDS is reused
-
-  // ---- add the wave pair's partials.  The pair splits the fragments: wk = 0
-  // keeps f = i * RN + j in [0, H), wk = 1 keeps [H, NF); each wave hands the
-  // other half to its partner through the (now idle) pipeline buffers, XR
-  // fragments per wave per round, and both then store their own half.
-  constexpr int NF = RM * RN;
-  constexpr int H = WK == 2 ? (NF + 1) / 2 : NF;
-  if (WK == 2) {
-    constexpr int XR = T::LDS_BYTES / (8 * 4096);
-    static_assert(XR >= 1, "LDS too small for the wave-pair exchange");
-    int32_t* xch = reinterpret_cast<int32_t*>(smem);
-    const int pair = wave & 3;
-    // slot of the k-th fragment sent in a round by wave (pair, sender wk)
-    const auto slot = [&](int k, int sender, int c) {
-      return xch + ((((k * 2 + sender) * 4 + pair) * 4 + c) * 64 + lane) * 4;
-    };
-#pragma unroll
-    for (int r0 = 0; r0 < H; r0 += XR) {
-      bare_barrier();  // the buffers are free (stage reads / previous round done)
-#pragma unroll
-      for (int k = 0; k < XR; ++k) {
-        const int fs0 = H + r0 + k, fs1 = r0 + k;  // what wk = 0 / wk = 1 sends
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (wk == 0 && fs0 < NF) {
-            const v16i& a = acc[fs0 / RN][fs0 % RN];
-            *reinterpret_cast<v4i*>(slot(k, 0, c)) = v4i{a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]};
-          }
-          if (wk == 1 && fs1 < H) {
-            const v16i& a = acc[fs1 / RN][fs1 % RN];
-            *reinterpret_cast<v4i*>(slot(k, 1, c)) = v4i{a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]};
-          }
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int k = 0; k < XR; ++k) {
-        const int fr0 = r0 + k, fr1 = H + r0 + k;  // what wk = 0 / wk = 1 receives
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (wk == 0 && fr0 < H) {
-            const v4i v = *reinterpret_cast<const v4i*>(slot(k, 1, c));
-            v16i& a = acc[fr0 / RN][fr0 % RN];
-            a[4 * c] += v.x;
-            a[4 * c + 1] += v.y;
-            a[4 * c + 2] += v.z;
-            a[4 * c + 3] += v.w;
-          }
-          if (wk == 1 && fr1 < NF) {
-            const v4i v = *reinterpret_cast<const v4i*>(slot(k, 0, c));
-            v16i& a = acc[fr1 / RN][fr1 % RN];
-            a[4 * c] += v.x;
-            a[4 * c + 1] += v.y;
-            a[4 * c + 2] += v.z;
-            a[4 * c + 3] += v.w;
-          }
-        }
-      }
-    }
-    __syncthreads();  // every wave is past the exchange buffers before they become transposes
-  } else {
-    __syncthreads();  // every wave is past its last stage before the buffers become transposes
-  }
-  const int f_lo = wk == 0 ? 0 : H, f_hi = wk == 0 ? H : NF;
-
-  if (p.splits > 1) {
-    // split-K: store this split's exact partial tile; splitk_reduce_kernel adds
-    // the splits and runs the epilogue.  Slot layout: fragment, 16-byte chunk,
-    // lane (each store instruction writes 1 KB contiguous).
-    int32_t* mine = p.ws_part + (static_cast<size_t>(w.tile) * p.splits + w.split) * T::SLOT_INTS;
-    const int pair = wave & 3;
-#pragma unroll
-    for (int i = 0; i < RM; ++i)
-#pragma unroll
-      for (int j = 0; j < RN; ++j) {
-        if (i * RN + j < f_lo || i * RN + j >= f_hi) continue;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const v4i v = {acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
-          *reinterpret_cast<v4i*>(mine + ((((pair * RM + i) * RN + j) * 4 + c) * 64 + lane) * 4) = v;
-        }
-      }
-    return;
-  }
-  // each wave transposes its fragments in its own 5 KB of the idle pipeline buffers
-  static_assert(T::LDS_BYTES >= 8 * 32 * kTrStride * 4, "LDS too small for the output transposes");
-  store_tile<RM, FN, OUT>(acc, p.out, row_scale, col_scale, M, N, m0, n0, wm, wn, lane,
-                          reinterpret_cast<int32_t*>(smem) + wave * 32 * kTrStride, f_lo, f_hi);
+  finish_tile<RM, FN, WK, WN, OUT>(acc, p, w, smem, row_scale, col_scale, wave, wk, lane);
 }
 
 // Split-K second pass: one workgroup per block tile, four waves in the same
@@ -658,7 +759,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tile = blockIdx.x;
-  const int m0 = (tile % p.tiles_m) * T::BM, n0 = (tile / p.tiles_m) * T::BN;
+  const int m0 = (tile % p.tiles_m) * T::BM, n0 = (tile / p.tiles_m) * p.tile_sn;
   if (OUT != kOutAcc) {
     for (int r = tid; r < T::BM; r += 256) row_scale[r] = p.a_scale[min(m0 + r, p.M - 1)];
     for (int c = tid; c < T::BN; c += 256) col_scale[c] = p.smax[min(n0 + c, p.N - 1)];
@@ -692,29 +793,36 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
 // ---------------------------------------------------------------- planner
 
 struct Plan {
-  int rm = 0, fn = 0, wk = 2, splits = 1, stages_per_split = 0, tiles_m = 0, tiles_n = 0;
+  int rm = 0, fn = 0, wk = 2, wn = 2, sn = 0, splits = 1, stages_per_split = 0, tiles_m = 0, tiles_n = 0;
   size_t slot_ints = 0;
 };
 
 struct Cfg {
-  int rm, fn, wk;
+  int rm, fn, wk, wn;
 };
-constexpr Cfg kCfgs[] = {{1, 4, 2}, {1, 8, 2}, {1, 10, 2}, {2, 4, 2}, {2, 5, 2},
-                         {2, 8, 2}, {2, 9, 2}, {2, 10, 2}, {4, 2, 2}, {4, 4, 2}};
+// (RM, FN, WK, WN): 2 WN WK waves.  The three-column-wave shapes (12 waves,
+// three per SIMD) exist for widths such as 17408 = 17 x 1024, where a
+// 128 x 288 tile advanced by 272 columns gives exactly 256 tiles.
+constexpr Cfg kCfgs[] = {{1, 4, 2, 2}, {1, 8, 2, 2}, {1, 10, 2, 2}, {2, 4, 2, 2}, {2, 5, 2, 2},
+                         {2, 8, 2, 2}, {2, 9, 2, 2}, {2, 10, 2, 2}, {4, 2, 2, 2}, {4, 4, 2, 2},
+                         {2, 9, 2, 3}};
 
-// Estimated cycles of one block tile on one CU.  Per 128-k stage and wave:
-// MFMA issue (32 cycles per 32x32x32, ~10% lost at one wave per SIMD), unpack
-// VALU (11 ops x 4 cycles per column fragment and k-step), LDS traffic
-// (fragment reads of all 4 waves plus the DMA writes, 128 B/clk) and L2->CU
-// traffic (64 B/clk); a stage costs the largest of these plus a fixed
-// barrier/wait overhead.  Then pipeline fill, epilogue stores and, with
-// split-K, the partial-tile traffic.
-double tile_cycles(int rm, int fn, int stages, int splits) {
-  const int rn = (fn + 1) / 2, bm = 64 * rm, bn = 32 * fn;
-  const double mfma = 4.0 * rm * rn * 32.0 * 1.1;
-  const double valu = 4.0 * rn * 9 * 4 + rn * 24.0 + 40.0;
+// Estimated cycles of one block tile on one CU.  Per 128-k stage and SIMD
+// (NW / 4 waves, each running 4 / WK k-steps of RM x RN MFMAs): MFMA issue
+// (32 cycles per 32x32x32, ~10% lost), unpack VALU (9 ops x 4 cycles per
+// column fragment and k-step, plus per-stage overhead), LDS traffic (fragment
+// reads of all waves plus the DMA writes, 128 B/clk) and L2->CU traffic
+// (64 B/clk); a stage costs the largest of these plus a fixed barrier/wait
+// overhead.  Then pipeline fill, epilogue stores and, with split-K, the
+// partial-tile traffic.
+double tile_cycles(int rm, int fn, int wn, int stages, int splits) {
+  const int rn = (fn + wn - 1) / wn, bm = 64 * rm, bn = 32 * fn;
+  const int nw = 4 * wn;                 // waves (WK = 2)
+  const double wps = nw / 4.0;           // waves per SIMD
+  const double mfma = wps * 2.0 * rm * rn * 32.0 * 1.1;
+  const double valu = wps * (2.0 * rn * 9 * 4 + rn * 12.0 + 20.0);
   const double dma = static_cast<double>(bm) * 128 + bn * 32.0;
-  const double lds = 4.0 * (4.0 * rm * 1024 + rn * 1024.0) / 128.0 + dma / 128.0;
+  const double lds = nw * (2.0 * rm * 1024 + rn * 512.0) / 128.0 + dma / 128.0;
   const double l2 = dma / 64.0;
   const double stage = std::max(std::max(mfma, valu), std::max(lds, l2)) + 250.0;
   double t = stages * stage + 2500.0 + bm * bn * 4.0 / 32.0;
@@ -726,40 +834,48 @@ double tile_cycles(int rm, int fn, int stages, int splits) {
   return t;
 }
 
-// Choose the block tile and split count that minimise the estimated makespan
-// (tiles are spread evenly, so the busiest CU runs ceil(units / CUs) tiles).
+// Choose the block tile, its column stride and the split count that minimise
+// the estimated makespan (tiles are spread evenly, so the busiest CU runs
+// ceil(units / CUs) tiles).  A stride 16 columns short of the tile width (the
+// last half fragment recomputed by the next tile) is tried as well; it and the
+// three-column-wave shapes are used without split-K only.
 Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
   Plan best;
   double best_t = 1e300;
   const int n_stages = static_cast<int>(K / kStageK);
   for (const Cfg& c : kCfgs) {
-    const int bm = 64 * c.rm, bn = 32 * c.fn, rn = (c.fn + 1) / 2;
-    const int64_t tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
-    for (int s = 1; s <= 32; ++s) {
-      const int sps = (n_stages + s - 1) / s;
-      const int splits = (n_stages + sps - 1) / sps;
-      if (splits != s) continue;
-      const int64_t units = tm * tn * splits;
-      if (units > (int64_t{1} << 31) - 1) continue;
-      if (static_cast<int64_t>(bn) * (((sps + 3) & ~3) + 4) > kQTileBytes) continue;
-      const int64_t rounds = (units + cus - 1) / cus;
-      const double tc = tile_cycles(c.rm, c.fn, sps, splits);
-      // makespan, plus a small charge for the total work (padding fragments,
-      // shared L2/HBM traffic) so that of two plans with the same number of
-      // rounds the one with fewer, fuller tiles wins
-      const double t = static_cast<double>(rounds) * tc +
-                       0.15 * tc * static_cast<double>(units) / cus *
-                           (static_cast<double>(2 * rn) / c.fn);
-      if (t < best_t * 0.995) {
-        best_t = t;
-        best.rm = c.rm;
-        best.fn = c.fn;
-        best.wk = c.wk;
-        best.splits = splits;
-        best.stages_per_split = sps;
-        best.tiles_m = static_cast<int>(tm);
-        best.tiles_n = static_cast<int>(tn);
-        best.slot_ints = static_cast<size_t>(4) * c.rm * rn * 64 * 16;
+    const int bm = 64 * c.rm, bn = 32 * c.fn, rn = (c.fn + c.wn - 1) / c.wn;
+    for (int sn : {bn, bn - 16}) {
+      const int64_t tm = (M + bm - 1) / bm, tn = (N + sn - 1) / sn;
+      for (int s = 1; s <= 32; ++s) {
+        if (s > 1 && (sn != bn || c.wn != 2)) break;
+        const int sps = (n_stages + s - 1) / s;
+        const int splits = (n_stages + sps - 1) / sps;
+        if (splits != s) continue;
+        const int64_t units = tm * tn * splits;
+        if (units > (int64_t{1} << 31) - 1) continue;
+        if (static_cast<int64_t>(bn) * (((sps + 3) & ~3) + 4) > kQTileBytes) continue;
+        const int64_t rounds = (units + cus - 1) / cus;
+        const double tc = tile_cycles(c.rm, c.fn, c.wn, sps, splits);
+        // makespan, plus a small charge for the total work (padding fragments,
+        // recomputed columns, shared L2/HBM traffic) so that of two plans with
+        // the same number of rounds the one with fewer, fuller tiles wins
+        const double t = static_cast<double>(rounds) * tc +
+                         0.15 * tc * static_cast<double>(units) / cus *
+                             (static_cast<double>(c.wn * rn) / c.fn) * (static_cast<double>(bn) / sn);
+        if (t < best_t * 0.995) {
+          best_t = t;
+          best.rm = c.rm;
+          best.fn = c.fn;
+          best.wk = c.wk;
+          best.wn = c.wn;
+          best.sn = sn;
+          best.splits = splits;
+          best.stages_per_split = sps;
+          best.tiles_m = static_cast<int>(tm);
+          best.tiles_n = static_cast<int>(tn);
+          best.slot_ints = static_cast<size_t>(2 * c.wn) * c.rm * rn * 64 * 16;
+        }
       }
     }
   }
@@ -772,24 +888,25 @@ size_t plan_workspace_bytes(const Plan& pl) {
   return tiles * pl.splits * pl.slot_ints * sizeof(int32_t);
 }
 
-template <int RM, int FN, int WK, int OUT>
+template <int RM, int FN, int WK, int WN, int OUT>
 hipError_t launch_cfg_out(const GemmArgs& a, hipStream_t stream) {
-  using T = Tile<RM, FN, WK>;
+  using T = Tile<RM, FN, WK, WN>;
   const unsigned tiles = static_cast<unsigned>(a.tiles_m) * a.tiles_n;
   const unsigned grid = tiles * a.splits;
-  hipLaunchKernelGGL((gemm_kernel<RM, FN, WK, OUT>), dim3(grid), dim3(T::THREADS), 0, stream, a);
+  hipLaunchKernelGGL((gemm_kernel<RM, FN, WK, WN, OUT>), dim3(grid), dim3(T::THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits <= 1) return e;
+  if (WN != 2) return hipErrorInvalidConfiguration;  // split-K is planned for WN = 2 only
   hipLaunchKernelGGL((splitk_reduce_kernel<RM, FN, OUT>), dim3(tiles), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int RM, int FN, int WK>
+template <int RM, int FN, int WK, int WN>
 hipError_t launch_cfg(const GemmArgs& a, OutKind out_kind, hipStream_t stream) {
   switch (out_kind) {
-    case kOutAcc: return launch_cfg_out<RM, FN, WK, kOutAcc>(a, stream);
-    case kOutBf16: return launch_cfg_out<RM, FN, WK, kOutBf16>(a, stream);
-    default: return launch_cfg_out<RM, FN, WK, kOutF32>(a, stream);
+    case kOutAcc: return launch_cfg_out<RM, FN, WK, WN, kOutAcc>(a, stream);
+    case kOutBf16: return launch_cfg_out<RM, FN, WK, WN, kOutBf16>(a, stream);
+    default: return launch_cfg_out<RM, FN, WK, WN, kOutF32>(a, stream);
   }
 }
 
@@ -809,9 +926,9 @@ hipError_t launch_gemm(const int8_t* x_i8, const float* a_scale, const uint8_t* 
   if (pl.rm == 0 || 32 * pl.fn * (((pl.stages_per_split + 3) & ~3) + 4) > kQTileBytes)
     return hipErrorInvalidConfiguration;  // no plan fits the q block in LDS
   if (std::getenv("TWL_LOG"))
-    std::fprintf(stderr, "[twl] gemm M=%lld N=%lld K=%lld -> tile %dx%d, %d waves, splits=%d (%d groups each) grid=%d\n",
+    std::fprintf(stderr, "[twl] gemm M=%lld N=%lld K=%lld -> tile %dx%d (stride %d), %d waves, splits=%d (%d groups each) grid=%d\n",
                  static_cast<long long>(M), static_cast<long long>(N), static_cast<long long>(K),
-                 64 * pl.rm, 32 * pl.fn, 4 * pl.wk, pl.splits, pl.stages_per_split,
+                 64 * pl.rm, 32 * pl.fn, pl.sn, 2 * pl.wn * pl.wk, pl.splits, pl.stages_per_split,
                  pl.tiles_m * pl.tiles_n * pl.splits);
   GemmArgs a;
   a.x = x_i8;
@@ -828,18 +945,21 @@ hipError_t launch_gemm(const int8_t* x_i8, const float* a_scale, const uint8_t* 
   a.tiles_n = pl.tiles_n;
   a.splits = pl.splits;
   a.stages_per_split = pl.stages_per_split;
-#define TWL_CFG(RM_, FN_, WK_) \
-  if (pl.rm == RM_ && pl.fn == FN_ && pl.wk == WK_) return launch_cfg<RM_, FN_, WK_>(a, out_kind, stream);
-  TWL_CFG(1, 4, 2)
-  TWL_CFG(1, 8, 2)
-  TWL_CFG(1, 10, 2)
-  TWL_CFG(2, 4, 2)
-  TWL_CFG(2, 5, 2)
-  TWL_CFG(2, 8, 2)
-  TWL_CFG(2, 9, 2)
-  TWL_CFG(2, 10, 2)
-  TWL_CFG(4, 2, 2)
-  TWL_CFG(4, 4, 2)
+  a.tile_sn = pl.sn;
+#define TWL_CFG(RM_, FN_, WK_, WN_)                                 \
+  if (pl.rm == RM_ && pl.fn == FN_ && pl.wk == WK_ && pl.wn == WN_) \
+    return launch_cfg<RM_, FN_, WK_, WN_>(a, out_kind, stream);
+  TWL_CFG(1, 4, 2, 2)
+  TWL_CFG(1, 8, 2, 2)
+  TWL_CFG(1, 10, 2, 2)
+  TWL_CFG(2, 4, 2, 2)
+  TWL_CFG(2, 5, 2, 2)
+  TWL_CFG(2, 8, 2, 2)
+  TWL_CFG(2, 9, 2, 2)
+  TWL_CFG(2, 10, 2, 2)
+  TWL_CFG(4, 2, 2, 2)
+  TWL_CFG(4, 4, 2, 2)
+  TWL_CFG(2, 9, 2, 3)
 #undef TWL_CFG
   return hipErrorInvalidValue;
 }

@@ -87,14 +87,15 @@ def _loops(body):
 
 def test_main_loop_has_one_wait_per_stage_and_no_accumulator_copies(asm):
     # the stage loop is unrolled by a whole number of pipeline stages: one
-    # vmcnt wait per stage (RM x ceil(FN/2) x 4/WK MFMAs), no AGPR copies
+    # vmcnt wait per stage (RM x ceil(FN/WN) x 4/WK MFMAs), no AGPR copies
     for name, body in _kernels(asm).items():
-        rm, fn, wk = (int(v) for v in re.search(r"gemm_kernelILi(\d+)ELi(\d+)ELi(\d+)E", name).groups())
+        rm, fn, wk, wn = (int(v) for v in
+                          re.search(r"gemm_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", name).groups())
         mains = [t for t in _loops(body).values() if "v_mfma" in t]
         assert len(mains) == 1, (name, len(mains))
         loop = mains[0]
         n_mfma = loop.count("v_mfma_i32_32x32x32_i8")
-        per_stage = rm * ((fn + 1) // 2) * (4 // wk)
+        per_stage = rm * ((fn + wn - 1) // wn) * (4 // wk)
         assert n_mfma > 0 and n_mfma % per_stage == 0, (name, n_mfma)
         assert loop.count("vmcnt") == n_mfma // per_stage, name
         assert "v_accvgpr" not in loop, name
