@@ -107,6 +107,58 @@ __device__ __forceinline__ void swap_halves(uint4& lo, uint4& hi) {
   hi = make_uint4(r0[1], r1[1], r2[1], r3[1]);
 }
 
+// Direct global->LDS loads for the activations of the row-balanced kernel.
+// Three 1 KB instructions (lane i writes LDS[lds + 1024 k + 16 i]) at address
+// sbase (wave-uniform, SGPR pair) + voff_k (per lane).  Issued from inline asm
+// so that the compiler does not drain vmcnt before every LDS read; the kernel
+// waits for them itself.  The LDS reads of the slot being refilled are
+// complete first (lgkmcnt(0)).
+__device__ __forceinline__ void dma16x3(const void* sbase, uint32_t v0, uint32_t v1, uint32_t v2,
+                                        uint32_t lds0, uint32_t lds1, uint32_t lds2) {
+  asm volatile(
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %0, %6\n\t"
+      "s_mov_b32 m0, %4\n\tglobal_load_lds_dwordx4 %1, %6\n\t"
+      "s_mov_b32 m0, %5\n\tglobal_load_lds_dwordx4 %2, %6"
+      :: "v"(v0), "v"(v1), "v"(v2), "s"(lds0), "s"(lds1), "s"(lds2), "s"(sbase) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] + vmcnt_hi[15:14], expcnt[6:4], lgkmcnt[11:8]
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ const void* sgpr_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)(p)));
+}
+
+// 16-byte chunk swizzle inside a 128-byte LDS row (distinct chunks for any 8
+// consecutive rows, so the column-wise 16-byte reads hit distinct banks).
+__device__ __forceinline__ int chunk_swizzle(int row) { return (row ^ (row >> 3)) & 7; }
+
+// Wait until at most `later` groups of PER loads each are outstanding (a
+// constant once the caller's loop is unrolled; later <= 4).
+template <int PER>
+__device__ __forceinline__ void wait_groups_after(int later) {
+  switch (later) {
+    case 1: wait_vmcnt<PER>(); break;
+    case 2: wait_vmcnt<2 * PER>(); break;
+    case 3: wait_vmcnt<3 * PER>(); break;
+    case 4: wait_vmcnt<4 * PER>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
 // MT is the exact number of tokens (1 .. 24).  A workgroup of nw waves covers
 // one 64-row block and one K slice; its waves split the slice's groups as
 // evenly as possible, at most GMAX each.  Static LDS: MT x 64 ints for the
@@ -338,17 +390,27 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(GemvArgs a, int M) {
 // work overlap.  Loads are issued unconditionally (slots past the wave's run
 // re-read its last group) so that the compiler's vmcnt waits stay static.
 // Lane (j, h) layout as in gemv_mfma_kernel.
+// The activations of a group (at most kXRows tokens x 128 bytes) go to LDS
+// by direct loads with 8 lanes per 128-byte row, so each 1 KB load touches 16
+// cache lines; read as MFMA operands (16 bytes of one token per lane) they
+// would touch 64 per instruction, and the address unit, not HBM, would bound
+// the kernel.  Each wave owns P slots, one per group in flight.
+constexpr int kXRows = 24;              // the decode paths take M <= 24
+constexpr int kXSlot = kXRows * 128;    // bytes per group slot
+constexpr int kRowsMaxWaves = 8;
+
 template <int NS>
 struct RowGroup {
   uint4 w[NS];   // 16 packed bytes of row 32 s + j, half h
-  v4i x[4];      // 64 activation bytes of token j, half h
   int q[NS];
 };
 
 template <int NS, int GMAX, int P, int MAXT>
 __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
   static_assert(P >= 1 && P <= GMAX, "prefetch depth");
+  static_assert(MAXT <= 64 * kRowsMaxWaves, "x slots are sized for 8 waves");
   __shared__ int red[32 * NS * kRedStride];
+  __shared__ __attribute__((aligned(1024))) int8_t xs[kRowsMaxWaves * P * kXSlot];
   __shared__ float row_scale[32];        // a_scale of the tokens
   __shared__ float col_scale[32 * NS];   // smax / 127 of the rows
   typedef int v16i __attribute__((ext_vector_type(16)));
@@ -389,8 +451,21 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
       wbase[s] = static_cast<size_t>(n >> 6) * G * 2048 + (n & 63) * 32 + h * 16;
       qrow[s] = a.q + static_cast<size_t>(n) * G;
     }
-    const int8_t* xrow = a.x + static_cast<size_t>(min(j, M - 1)) * K + h * 64;
+    // activation DMA: instruction i, lane l -> LDS row r = 8 i + l / 8 (token
+    // min(r, M - 1)), LDS chunk l % 8 holding global chunk (l % 8) ^ swizzle(r)
+    uint32_t xoff[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      xoff[i] = static_cast<uint32_t>(min(r, M - 1) * K + 16 * ((lane & 7) ^ chunk_swizzle(r)));
+    }
+    const void* xbase = sgpr_ptr(a.x);
+    const uint32_t xs_wave = lds_addr(xs) + static_cast<uint32_t>(wave * P * kXSlot);
+    // this lane's operand row in a slot (tokens past kXRows are never reduced)
+    const int jr = min(j, kXRows - 1);
 
+    // per group: NS weight loads and NS q loads (VGPR), then the 3 activation
+    // DMAs; the activation wait below counts on exactly this order
     RowGroup<NS> buf[P];
     auto issue = [&](RowGroup<NS>& d, int jj) {
       const int g = g0 + min(jj, ng - 1);
@@ -398,10 +473,10 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
       for (int s = 0; s < NS; ++s)
         d.w[s] = *reinterpret_cast<const uint4*>(a.packed + wbase[s] + static_cast<size_t>(g) * 2048);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        d.x[t] = *reinterpret_cast<const v4i*>(xrow + static_cast<size_t>(g) * 128 + 16 * t);
-#pragma unroll
       for (int s = 0; s < NS; ++s) d.q[s] = qrow[s][g];
+      const uint32_t slot = __builtin_amdgcn_readfirstlane(xs_wave + (jj % P) * kXSlot);
+      const uint32_t gx = static_cast<uint32_t>(g) * 128;
+      dma16x3(xbase, xoff[0] + gx, xoff[1] + gx, xoff[2] + gx, slot, slot + 1024, slot + 2048);
     };
 #pragma unroll
     for (int jj = 0; jj < P; ++jj) issue(buf[jj], jj);
@@ -412,14 +487,24 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
 #pragma unroll
     for (int jj = 0; jj < GMAX; ++jj) {
       RowGroup<NS>& d = buf[jj % P];
+      // this group's activation DMAs are done once at most the loads of the
+      // groups issued after it are outstanding (2 NS + 3 per group; counting
+      // 2 NS + 1 only makes the wait stricter)
+      wait_groups_after<2 * NS + 1>(min(P - 1, GMAX - 1 - jj));
+      asm volatile("" ::: "memory");
       if (jj == 0 || jj < ng) {
+        const int8_t* xr = xs + (wave * P + jj % P) * kXSlot + jr * 128;
+        v4i xv[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          xv[t] = *reinterpret_cast<const v4i*>(xr + 16 * ((4 * h + t) ^ chunk_swizzle(jr)));
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const QTables tab = make_tables(d.q[s]);
           const uint32_t wv[4] = {d.w[s].x, d.w[s].y, d.w[s].z, d.w[s].w};
 #pragma unroll
           for (int t = 0; t < 4; ++t)
-            acc[s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(wv[t], tab), d.x[t], acc[s], 0, 0, 0);
+            acc[s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(wv[t], tab), xv[t], acc[s], 0, 0, 0);
         }
       }
       if (jj + P < GMAX) issue(d, jj + P);
