@@ -29,13 +29,15 @@
 //   (v_permlane32_swap) gives each lane its row's 8 words, then 4 v_dot4 per
 //   word and token, with the activations read at wave-uniform addresses
 //   through the constant address space (scalar loads, one copy per wave).
-//   Its VALU work grows with M: it is used for M < 4.
-// MFMA kernels (4 <= M <= 24): the tokens padded to 32 form the B operand of
+//   Its VALU work grows with M: it is used for M < 4 on layers too narrow
+//   for the row-balanced kernel.
+// MFMA kernels: the tokens padded to 32 form the B operand of
 //   v_mfma_i32_32x32x32_i8 and the unpacked weights the A operand, which makes
 //   the work nearly independent of M.  gemv_rows_kernel gives every CU an
 //   equal contiguous range of rows over all of K (no partial sums leave the
-//   workgroup); gemv_mfma_kernel keeps the 64-row-block split with K slices,
-//   for layers with too few rows per CU.
+//   workgroup) and is used at every M whenever each CU gets at least 16 rows;
+//   gemv_mfma_kernel keeps the 64-row-block split with K slices (4 <= M <= 24)
+//   for layers with fewer rows per CU.
 #include "twl_internal.h"
 
 #include <algorithm>
@@ -113,14 +115,28 @@ __device__ __forceinline__ void swap_halves(uint4& lo, uint4& hi) {
 // so that the compiler does not drain vmcnt before every LDS read; the kernel
 // waits for them itself.  The LDS reads of the slot being refilled are
 // complete first (lgkmcnt(0)).
-__device__ __forceinline__ void dma16x3(const void* sbase, uint32_t v0, uint32_t v1, uint32_t v2,
+// `n` (1 .. 3, wave-uniform) instructions are issued: tokens 8 n .. 23 of a
+// slot are not loaded when M <= 8 n.
+__device__ __forceinline__ void dma16xn(int n, const void* sbase, uint32_t v0, uint32_t v1, uint32_t v2,
                                         uint32_t lds0, uint32_t lds1, uint32_t lds2) {
-  asm volatile(
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "s_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %0, %6\n\t"
-      "s_mov_b32 m0, %4\n\tglobal_load_lds_dwordx4 %1, %6\n\t"
-      "s_mov_b32 m0, %5\n\tglobal_load_lds_dwordx4 %2, %6"
-      :: "v"(v0), "v"(v1), "v"(v2), "s"(lds0), "s"(lds1), "s"(lds2), "s"(sbase) : "memory", "m0");
+  if (n >= 3)
+    asm volatile(
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "s_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %0, %6\n\t"
+        "s_mov_b32 m0, %4\n\tglobal_load_lds_dwordx4 %1, %6\n\t"
+        "s_mov_b32 m0, %5\n\tglobal_load_lds_dwordx4 %2, %6"
+        :: "v"(v0), "v"(v1), "v"(v2), "s"(lds0), "s"(lds1), "s"(lds2), "s"(sbase) : "memory", "m0");
+  else if (n == 2)
+    asm volatile(
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %4\n\t"
+        "s_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %4"
+        :: "v"(v0), "v"(v1), "s"(lds0), "s"(lds1), "s"(sbase) : "memory", "m0");
+  else
+    asm volatile(
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, %2"
+        :: "v"(v0), "s"(lds0), "s"(sbase) : "memory", "m0");
 }
 
 template <int N>
@@ -402,7 +418,6 @@ constexpr int kRowsMaxWaves = 8;
 template <int NS>
 struct RowGroup {
   uint4 w[NS];   // 16 packed bytes of row 32 s + j, half h
-  int q[NS];
 };
 
 template <int NS, int GMAX, int P, int MAXT>
@@ -412,7 +427,7 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
   __shared__ int red[32 * NS * kRedStride];
   __shared__ __attribute__((aligned(1024))) int8_t xs[kRowsMaxWaves * P * kXSlot];
   __shared__ float row_scale[32];        // a_scale of the tokens
-  __shared__ float col_scale[32 * NS];   // smax / 127 of the rows
+  __shared__ float col_scale[32 * NS];   // smax of the rows
   typedef int v16i __attribute__((ext_vector_type(16)));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -430,13 +445,15 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
   const int ng = ((wave + 1) * G) / nw - g0;  // 0 .. GMAX
 
   // the epilogue's scales, loaded by the last wave now and used after the
-  // main loop, so that their latency hides behind the weight stream
+  // main loop, so that their latency hides behind the weight stream (clamped
+  // indices and no per-lane branch: a divergent load here made the compiler
+  // wait for it before the stream was issued)
   const bool scale_wave = wave == nw - 1 && a.out_kind != kOutAcc;
   float sc_row = 0.0f, sc_col0 = 0.0f, sc_col1 = 0.0f;
   if (scale_wave) {
-    if (lane < M) sc_row = a.a_scale[lane];
-    if (lane < R) sc_col0 = a.smax[r0 + lane];
-    if (lane + 64 < R) sc_col1 = a.smax[r0 + lane + 64];
+    sc_row = a.a_scale[min(lane, M - 1)];
+    sc_col0 = a.smax[r0 + min(lane, R - 1)];
+    sc_col1 = a.smax[r0 + min(lane + 64, R - 1)];
   }
 
   if (ng > 0) {
@@ -444,15 +461,47 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
     // lanes past the last row of this workgroup re-read that row: the same
     // cache lines, so no bytes beyond the workgroup's own rows are fetched
     size_t wbase[NS];
-    const int8_t* qrow[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int n = min(r0 + 32 * s + j, r1 - 1);
       wbase[s] = static_cast<size_t>(n >> 6) * G * 2048 + (n & 63) * 32 + h * 16;
-      qrow[s] = a.q + static_cast<size_t>(n) * G;
     }
+    // q of this lane's rows for all of the wave's groups: QD dwords from the
+    // 4-aligned start q[n, g0 & ~3] (rows of q are G bytes, G % 8 == 0, so no
+    // dword straddles a row end; dwords past the row end are clamped), loaded
+    // once up front instead of one byte gather per group
+    // (held in vector registers: as a plain array the compiler may move it to
+    // LDS, which then waits on the loads before the other groups are issued)
+    constexpr int QD = GMAX / 4 + 2;
+    constexpr int QV = QD <= 4 ? 4 : (QD <= 8 ? 8 : 16);
+    static_assert(QD <= QV, "q dwords");
+    typedef uint32_t qvec __attribute__((ext_vector_type(QV)));
+    const int qa = g0 & ~3, qsh = g0 & 3;
+    const int qd_last = (G - qa) / 4 - 1;
+    qvec qw0 = {}, qw1 = {}, qw2 = {};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int n = min(r0 + 32 * s + j, r1 - 1);
+      const uint32_t* qrow = reinterpret_cast<const uint32_t*>(a.q + static_cast<size_t>(n) * G + qa);
+      qvec v = {};
+#pragma unroll
+      for (int d = 0; d < QD; ++d) v[d] = qrow[min(d, qd_last)];
+      if (s == 0) qw0 = v;
+      else if (s == 1) qw1 = v;
+      else qw2 = v;
+    }
+    static_assert(NS <= 3, "q vectors for at most 3 subtiles");
+    // q[n, g0 + jj]: byte qsh + jj of the run (jj is a constant once unrolled):
+    // a 64-bit shift of two dwords picked by constant indices
+    const auto qbyte = [&](int s, int jj) {
+      const qvec& v = s == 0 ? qw0 : (s == 1 ? qw1 : qw2);
+      const uint64_t w = (static_cast<uint64_t>(v[(jj >> 2) + 1]) << 32) | v[jj >> 2];
+      return static_cast<int>(static_cast<int8_t>(w >> (8 * (qsh + (jj & 3)))));
+    };
     // activation DMA: instruction i, lane l -> LDS row r = 8 i + l / 8 (token
-    // min(r, M - 1)), LDS chunk l % 8 holding global chunk (l % 8) ^ swizzle(r)
+    // min(r, M - 1)), LDS chunk l % 8 holding global chunk (l % 8) ^ swizzle(r);
+    // xi = ceil(M / 8) instructions per group
+    const int xi = (M + 7) >> 3;
     uint32_t xoff[3];
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
@@ -464,19 +513,17 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
     // this lane's operand row in a slot (tokens past kXRows are never reduced)
     const int jr = min(j, kXRows - 1);
 
-    // per group: NS weight loads and NS q loads (VGPR), then the 3 activation
-    // DMAs; the activation wait below counts on exactly this order
+    // per group: NS weight loads (VGPR), then the xi activation DMAs; the
+    // activation wait below counts on exactly this order
     RowGroup<NS> buf[P];
     auto issue = [&](RowGroup<NS>& d, int jj) {
       const int g = g0 + min(jj, ng - 1);
 #pragma unroll
       for (int s = 0; s < NS; ++s)
         d.w[s] = *reinterpret_cast<const uint4*>(a.packed + wbase[s] + static_cast<size_t>(g) * 2048);
-#pragma unroll
-      for (int s = 0; s < NS; ++s) d.q[s] = qrow[s][g];
       const uint32_t slot = __builtin_amdgcn_readfirstlane(xs_wave + (jj % P) * kXSlot);
       const uint32_t gx = static_cast<uint32_t>(g) * 128;
-      dma16x3(xbase, xoff[0] + gx, xoff[1] + gx, xoff[2] + gx, slot, slot + 1024, slot + 2048);
+      dma16xn(xi, xbase, xoff[0] + gx, xoff[1] + gx, xoff[2] + gx, slot, slot + 1024, slot + 2048);
     };
 #pragma unroll
     for (int jj = 0; jj < P; ++jj) issue(buf[jj], jj);
@@ -488,9 +535,9 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
     for (int jj = 0; jj < GMAX; ++jj) {
       RowGroup<NS>& d = buf[jj % P];
       // this group's activation DMAs are done once at most the loads of the
-      // groups issued after it are outstanding (2 NS + 3 per group; counting
-      // 2 NS + 1 only makes the wait stricter)
-      wait_groups_after<2 * NS + 1>(min(P - 1, GMAX - 1 - jj));
+      // groups issued after it are outstanding (NS + xi per group; counting
+      // NS + 1 only makes the wait stricter)
+      wait_groups_after<NS + 1>(min(P - 1, GMAX - 1 - jj));
       asm volatile("" ::: "memory");
       if (jj == 0 || jj < ng) {
         const int8_t* xr = xs + (wave * P + jj % P) * kXSlot + jr * 128;
@@ -500,7 +547,7 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
           xv[t] = *reinterpret_cast<const v4i*>(xr + 16 * ((4 * h + t) ^ chunk_swizzle(jr)));
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const QTables tab = make_tables(d.q[s]);
+          const QTables tab = make_tables(qbyte(s, jj));
           const uint32_t wv[4] = {d.w[s].x, d.w[s].y, d.w[s].z, d.w[s].w};
 #pragma unroll
           for (int t = 0; t < 4; ++t)
@@ -523,8 +570,8 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
   }
   if (scale_wave) {
     if (lane < M) row_scale[lane] = sc_row;
-    if (lane < R) col_scale[lane] = sc_col0 * (1.0f / 127.0f);
-    if (lane + 64 < R) col_scale[lane + 64] = sc_col1 * (1.0f / 127.0f);
+    if (lane < R) col_scale[lane] = sc_col0;
+    if (lane + 64 < R) col_scale[lane + 64] = sc_col1;
   }
   __syncthreads();
 
@@ -533,7 +580,8 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
     const int sum = red[rr * kRedStride + t];
     const size_t o = static_cast<size_t>(t) * N + r0 + rr;
     store_out(a.out, o, a.out_kind, sum,
-              a.out_kind == kOutAcc ? 0.0f : static_cast<float>(sum) * row_scale[t] * col_scale[rr]);
+              a.out_kind == kOutAcc ? 0.0f
+                                    : static_cast<float>(sum) * row_scale[t] * (col_scale[rr] * (1.0f / 127.0f)));
   }
 }
 
@@ -621,11 +669,12 @@ constexpr int kRowsGmaxChoices[] = {3, 5, 9, 17, 33};
 
 // Row-balanced plan: an even share of rows for every CU (a multiple of the CU
 // count of workgroups), at most 3 subtiles of 32 rows each, the whole of K
-// split over the waves.  Every workgroup reads all of x_i8 (M x K bytes) next
-// to its R x K / 4 bytes of weights, so the plan is only taken when each
-// workgroup has at least 40 rows; with fewer (the 17408 -> 5120 layer has 20
-// per CU) the K-split kernel, which shares each activation chunk among 64
-// rows, was measured faster despite its second launch.
+// split over the waves.  Every workgroup reads all of x_i8 (M x K bytes, by
+// coalesced direct loads into LDS) next to its R x K / 4 bytes of weights; the
+// plan is taken when each workgroup has at least 16 rows.  Measured against
+// the K-split kernel and its second launch: 17408 -> 5120 (20 rows per CU)
+// 10.1 against 12.1 us at M = 4, 13.6 against 15.2 us at M = 24; and, for
+// these shapes, faster than the dot4 kernel from M = 1 on.
 GemvPlan make_rows_plan(int64_t N, int64_t K, const DeviceInfo& dev) {
   GemvPlan p;
   p.slices = 0;
@@ -634,7 +683,7 @@ GemvPlan make_rows_plan(int64_t N, int64_t K, const DeviceInfo& dev) {
   const int64_t per_round = static_cast<int64_t>(cus) * 96;
   const int64_t rounds = (N + per_round - 1) / per_round;
   const int64_t wgs = rounds * cus;
-  if (N < 40 * wgs) return p;
+  if (N < 16 * wgs) return p;
   const int64_t rmax = (N + wgs - 1) / wgs;
   p.rows_ns = static_cast<int>((rmax + 31) / 32);
   p.rows_wgs = static_cast<int>(wgs);
@@ -652,11 +701,16 @@ GemvPlan make_rows_plan(int64_t N, int64_t K, const DeviceInfo& dev) {
 
 // Always returns a valid plan for 1 <= M <= 24 and K <= the library's limit:
 // the dot4 kernel takes up to 16 waves x 9 groups x 32 slices.
+// Automatic choice: the row-balanced matrix-core kernel whenever its plan
+// applies (at every M), else the dot4 kernel below kMfmaMinM tokens and the
+// K-split matrix-core kernel from there on.
 GemvPlan make_plan(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceInfo& dev) {
-  const bool want_mfma = kind == kGemvMfma || (kind == kGemvAuto && M >= kMfmaMinM);
-  if (want_mfma && M <= 32) {
+  if (kind != kGemvDot4 && M <= 32) {
     const GemvPlan r = make_rows_plan(N, K, dev);
     if (r.slices > 0) return r;
+  }
+  const bool want_mfma = kind == kGemvMfma || (kind == kGemvAuto && M >= kMfmaMinM);
+  if (want_mfma && M <= 32) {
     const GemvPlan p = make_plan_for(M, N, K, dev, true);
     if (p.slices > 0) return p;
   }
@@ -682,6 +736,7 @@ hipError_t launch_rows_ns(GemvArgs a, int M, const GemvPlan& pl, hipStream_t str
 
 hipError_t launch_rows(GemvArgs a, int M, const GemvPlan& pl, hipStream_t stream) {
   switch (pl.rows_ns) {
+    case 1: return launch_rows_ns<1, 512>(a, M, pl, stream);
     case 2: return launch_rows_ns<2, 512>(a, M, pl, stream);
     case 3: return launch_rows_ns<3, 512>(a, M, pl, stream);
     default: return hipErrorInvalidValue;

@@ -161,7 +161,10 @@ def test_gemm_ragged_shapes(twl, M, N, K):
 @pytest.mark.parametrize("N,K", [(1, 1024), (65, 2048), (1000, 5120),
                                  # row-balanced decode: 40-41 rows per workgroup,
                                  # 95-96 rows, and two rounds of workgroups (48 rows)
-                                 (10241, 2048), (24575, 1024), (24577, 1024)])
+                                 (10241, 2048), (24575, 1024), (24577, 1024),
+                                 # one 32-row subtile: 16-17 rows per workgroup with
+                                 # 3 groups per wave, 31-32 rows with 9 groups per wave
+                                 (4100, 3072), (8000, 9216)])
 def test_gemv_vs_gemm_shapes(twl, M, N, K):
     # every decode kernel (automatic choice, dot4, MFMA) and the GEMM against
     # the oracle, bit-exact in acc
