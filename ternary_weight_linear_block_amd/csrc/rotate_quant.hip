@@ -217,24 +217,43 @@ __global__ __launch_bounds__(1024) void rotate_quant_kernel(
   // rint(|v| <= tiny) = 0 without a branch per element
   const float div = scale > 0.0f ? scale : 1.0f;
   int8_t* yr = x_i8 + static_cast<size_t>(t) * K;
+  // The quotient v / div must be the IEEE-rounded one (the quantiser rounds
+  // it to the nearest integer, ties to even).  With inv = RN(1 / div), one
+  // IEEE division per token, q0 = RN(v inv) is within one ulp of v / div, the
+  // residual v - q0 div is exact in one fma, and RN(q0 + residual * inv) is
+  // the correctly rounded quotient (Markstein's theorem), as long as nothing
+  // overflows or underflows: 3 operations per element instead of the ~11 of a
+  // full division.  Quotients that underflow are far below 1/2 and round to 0
+  // either way; a scale below 2^-64 (inv near overflow) keeps the division.
+  const bool markstein = div >= 0x1p-64f;  // uniform across the workgroup
+  const float inv = 1.0f / div;            // IEEE division
+  const auto quant = [&](float q) {
+    const float r = fminf(fmaxf(rintf(q), -127.0f), 127.0f);  // ties to even
+    return static_cast<uint32_t>(static_cast<int>(r)) & 0xFFu;
+  };
+  const auto store_all = [&](auto quotient) {
 #pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int b = wave + i * nw;
-    if (b < nblocks) {
+    for (int i = 0; i < BPW; ++i) {
+      const int b = wave + i * nw;
+      if (b < nblocks) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint32_t word = 0;
+        for (int c = 0; c < 4; ++c) {
+          uint32_t word = 0;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          float r = rintf(v[i][4 * c + d] / div);  // IEEE division, ties to even
-          r = fminf(fmaxf(r, -127.0f), 127.0f);
-          const int qv = static_cast<int>(r);
-          word |= (static_cast<uint32_t>(qv) & 0xFFu) << (8 * d);
+          for (int d = 0; d < 4; ++d) word |= quant(quotient(v[i][4 * c + d])) << (8 * d);
+          *reinterpret_cast<uint32_t*>(yr + b * kBlock + 256 * c + 4 * lane) = word;
         }
-        *reinterpret_cast<uint32_t*>(yr + b * kBlock + 256 * c + 4 * lane) = word;
       }
     }
-  }
+  };
+  // the test is hoisted out of the element loop (one branch per token)
+  if (markstein)
+    store_all([&](float w) {
+      const float q0 = w * inv;
+      return __builtin_fmaf(__builtin_fmaf(-q0, div, w), inv, q0);
+    });
+  else
+    store_all([&](float w) { return w / div; });
 }
 
 template <int BPW, bool SILU, bool RAW>
