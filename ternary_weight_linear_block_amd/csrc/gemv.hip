@@ -514,13 +514,17 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
     const int jr = min(j, kXRows - 1);
 
     // per group: NS weight loads (VGPR), then the xi activation DMAs; the
-    // activation wait below counts on exactly this order
+    // activation wait below counts on exactly this order.  The weights are
+    // read once per call: nontemporal loads (measured 2-3% faster)
     RowGroup<NS> buf[P];
     auto issue = [&](RowGroup<NS>& d, int jj) {
       const int g = g0 + min(jj, ng - 1);
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
-        d.w[s] = *reinterpret_cast<const uint4*>(a.packed + wbase[s] + static_cast<size_t>(g) * 2048);
+      for (int s = 0; s < NS; ++s) {
+        const u32x4 t = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(a.packed + wbase[s] + static_cast<size_t>(g) * 2048));
+        d.w[s] = make_uint4(t.x, t.y, t.z, t.w);
+      }
       const uint32_t slot = __builtin_amdgcn_readfirstlane(xs_wave + (jj % P) * kXSlot);
       const uint32_t gx = static_cast<uint32_t>(g) * 128;
       dma16xn(xi, xbase, xoff[0] + gx, xoff[1] + gx, xoff[2] + gx, slot, slot + 1024, slot + 2048);
