@@ -195,8 +195,9 @@ struct GemmArgs {
   int32_t* ws_part;    // [tiles][splits][SLOT_INTS] split-K partial tiles
   int M, N, K;
   int tiles_m, tiles_n, splits, stages_per_split;
-  int tile_sn;         // column stride between block tiles (<= BN; a tile
-                       // computes BN columns and stores the first tile_sn)
+  int tile_sn;         // column stride between block tiles: a tile computes
+                       // BN columns and stores the first tile_sn (the
+                       // planner sets tile_sn = BN)
 };
 
 // Writes one wave's RM x RN fragments of the output tile: fp32 y with the
@@ -840,18 +841,18 @@ double tile_cycles(int rm, int fn, int wn, int stages, int splits) {
   return t;
 }
 
-// Choose the block tile, its column stride and the split count that minimise
-// the estimated makespan (tiles are spread evenly, so the busiest CU runs
-// ceil(units / CUs) tiles).  A stride 16 columns short of the tile width (the
-// last half fragment recomputed by the next tile) is tried as well; it and the
-// three-column-wave shapes are used without split-K only.
+// Choose the block tile and the split count that minimise the estimated
+// makespan (tiles are spread evenly, so the busiest CU runs ceil(units / CUs)
+// tiles).  Tiles advance by their full width (a stride 16 columns short, the
+// last half fragment recomputed by the next tile, was measured no faster for
+// N = 17408); the three-column-wave shapes are used without split-K only.
 Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
   Plan best;
   double best_t = 1e300;
   const int n_stages = static_cast<int>(K / kStageK);
   for (const Cfg& c : kCfgs) {
     const int bm = 64 * c.rm, bn = 32 * c.fn, rn = (c.fn + c.wn - 1) / c.wn;
-    for (int sn : {bn, bn - 16}) {
+    for (int sn : {bn}) {
       const int64_t tm = (M + bm - 1) / bm, tn = (N + sn - 1) / sn;
       for (int s = 1; s <= 32; ++s) {
         if (s > 1 && (sn != bn || c.wn != 2)) break;
