@@ -22,16 +22,17 @@
 //     pipeline stage (one scale group), lane half h at k-step s covers
 //     k = 16 (4 h + s) .. +15, so a lane's B data for a whole stage is 16
 //     contiguous packed bytes (4 words) and its scale is q[n, g].
-//   * Workgroup: 8 waves, two per SIMD.  Block tile BM = 64 RM rows x
-//     BN = 32 FN columns split 2 along M x 2 along N; wave (wm, wn) owns RM row
-//     fragments and ceil(FN/2) column fragments (an odd FN leaves wn=1 one
-//     padding fragment), and the two waves (wk = 0, 1) of each (wm, wn) take
-//     k-steps {0,1} and {2,3} of every stage.  At the end the pair splits the
-//     tile's fragments in half and each wave adds its partner's int32
-//     partials for its half through LDS (exact), so all 8 waves store.  Two
-//     waves per SIMD let one wave's unpack VALU and LDS reads run while the
-//     other's MFMAs execute; with one wave per SIMD these costs were measured
-//     to add up.
+//   * Workgroup: 2 WN x 2 waves (8 for WN = 2, two per SIMD; 12 for WN = 3,
+//     three per SIMD).  Block tile BM = 64 RM rows x BN = 32 FN columns split
+//     2 along M x WN along N; wave (wm, wn) owns RM row fragments and
+//     ceil(FN/WN) column fragments (a remainder leaves the last wn padding
+//     fragments), and the two waves (wk = 0, 1) of each (wm, wn) take k-steps
+//     {0,1} and {2,3} of every stage.  At the end the pair splits the output
+//     by fragment rows (accumulator registers 0-7 / 8-15) and each wave adds
+//     its partner's int32 partials for its half through LDS (exact), so all
+//     waves store.  With two or more waves per SIMD one wave's unpack VALU
+//     and LDS reads run while another's MFMAs execute (the MFMA clusters run
+//     at raised wave priority).
 //   * Multi-stage pipeline (4 stages; 3 for 256-row tiles) of direct
 //     global->LDS loads (global_load_lds dwordx4: no VGPR staging).  A stage
 //     holds BM x 128 bytes of x_i8 (8 lanes per row; 16-byte chunks
@@ -53,10 +54,11 @@
 //     same weights) land on the same XCD and its L2.
 //   * The stage loop is unrolled by the pipeline depth, so buffer offsets are
 //     constants and the packed words alternate between two register sets.
-//   * Output: each 32x32 fragment is transposed through a per-wave LDS scratch
-//     so that every lane writes 16 contiguous bytes (fp32 / int32 y: 4
-//     columns; bf16 y: 8 columns): the output phase is bound by the number of
-//     store transactions, not by bytes.
+//   * Output: each kept 16x32 half fragment is transposed through a per-wave
+//     LDS scratch (two buffers, alternated) so that every lane writes 16
+//     contiguous bytes (fp32 / int32 y: 4 columns; bf16 y: 8 columns): the
+//     output phase is bound by the number of store transactions, not by
+//     bytes.
 #include "twl_internal.h"
 
 #include <algorithm>

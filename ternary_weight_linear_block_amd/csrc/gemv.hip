@@ -395,7 +395,7 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(GemvArgs a, int M) {
   }
 }
 
-// Row-balanced matrix-core decode (M <= 32 tokens, N >= 16 rows per CU).
+// Row-balanced matrix-core decode (M <= 24 tokens, N >= 16 rows per CU).
 // Streaming is bound per CU, so each workgroup takes an equal contiguous range
 // of rows [r0, r1) (any length up to 32 NS) over the whole of K: every CU
 // streams the same number of bytes and no partial sums leave the workgroup.
@@ -709,7 +709,7 @@ GemvPlan make_rows_plan(int64_t N, int64_t K, const DeviceInfo& dev) {
 // applies (at every M), else the dot4 kernel below kMfmaMinM tokens and the
 // K-split matrix-core kernel from there on.
 GemvPlan make_plan(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceInfo& dev) {
-  if (kind != kGemvDot4 && M <= 32) {
+  if (kind != kGemvDot4 && M <= kXRows) {
     const GemvPlan r = make_rows_plan(N, K, dev);
     if (r.slices > 0) return r;
   }
@@ -810,7 +810,7 @@ hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* 
   a.out_kind = out_kind;
   hipError_t e = hipErrorInvalidValue;
   if (pl.rows_ns > 0) {
-    if (M > 32 || pl.nw * 64 > 512) return hipErrorInvalidValue;
+    if (M > kXRows || pl.nw * 64 > 512) return hipErrorInvalidValue;  // x slots hold kXRows tokens
     e = launch_rows(a, static_cast<int>(M), pl, stream);
   } else if (pl.mfma) {
     if (M > 32 || pl.nw * 64 > (pl.gmax <= 3 ? 1024 : 512)) return hipErrorInvalidValue;
