@@ -59,7 +59,7 @@ typedef enum {
 typedef enum {
   TWL_PATH_AUTO = 0,       /* decode kernel for M <= TWL_GEMV_MAX_M, else the GEMM */
   TWL_PATH_GEMM = 1,       /* int8-MFMA GEMM with in-register 2-bit unpack         */
-  TWL_PATH_GEMV = 2,       /* decode kernel (M <= TWL_GEMV_MAX_M), chosen by M     */
+  TWL_PATH_GEMV = 2,       /* decode kernel (M <= TWL_GEMV_MAX_M), chosen by shape */
   TWL_PATH_GEMV_DOT4 = 3,  /* decode: packed-2-bit dot4 GEMV, no matrix cores      */
   TWL_PATH_GEMV_MFMA = 4   /* decode: 32-token-padded int8 MFMA over the stream    */
 } twl_path;
@@ -148,7 +148,9 @@ size_t twl_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   y[t,n]   = acc[t,n] * a_scale[t] * smax[n] / 127           (fp32)
  *   Prefill sizes run an int8-MFMA GEMM that unpacks the 2-bit codes on chip;
  *   decode batches (M <= TWL_GEMV_MAX_M) stream the packed weights through a
- *   dot4 GEMV (M < 4) or a 32-token-padded int8 MFMA kernel.  All give
+ *   32-token-padded int8 MFMA kernel (every CU an equal range of rows when
+ *   each CU gets at least 16 rows) or, for narrower layers, a dot4 GEMV
+ *   (M < 4) or a K-split MFMA kernel.  All give
  *   bit-identical acc.
  *   x_i8 [M,K], a_scale [M], packed (twl_packed_bytes(N,K) bytes), q [N,K/128],
  *   smax [N] as produced by the two calls above; y out: fp32 [M, N].
@@ -206,8 +208,11 @@ typedef enum {
  * The bf16 output halves the bytes of y, which dominate the prefill step's
  * traffic (the pages' consumers take bf16 activations, [P1] section 4).
  * The decode paths (TWL_PATH_GEMV, _GEMV_DOT4, _GEMV_MFMA) require
- * M <= TWL_GEMV_MAX_M; TWL_PATH_GEMV picks the dot4 kernel for the smallest
- * batches and the MFMA kernel above.  All paths give bit-identical acc.
+ * M <= TWL_GEMV_MAX_M; TWL_PATH_GEMV picks the row-balanced MFMA kernel
+ * when each CU gets at least 16 rows, else the dot4 kernel for M < 4 and the
+ * K-split MFMA kernel above.  TWL_PATH_GEMV_MFMA forces a matrix-core decode
+ * kernel (row-balanced when it applies) and TWL_PATH_GEMV_DOT4 the dot4
+ * kernel.  All paths give bit-identical acc.
  */
 twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
                                  const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
