@@ -364,9 +364,12 @@ def test_reference_linear_bf16(twl, M, N, K, rows):
 # ------------------------------------------------------ HIP graph replays
 
 @pytest.mark.parametrize("M,N,K", [(512, 1000, 5120),    # GEMM
+                                   (512, 17408, 1024),   # GEMM, 12-wave 128x288 tiles
                                    (40, 300, 32768),     # GEMM with split-K partials
                                    (9, 200, 20480),      # MFMA decode, K slices + reduce
                                    (5, 24575, 1024),     # row-balanced MFMA decode
+                                   (1, 5120, 17408),     # row-balanced, one subtile, 17 groups/wave
+                                   (24, 17408, 5120),    # row-balanced, three subtiles, 24 tokens
                                    (2, 1000, 5120)])     # dot4 decode
 def test_graph_replays_match_eager(twl, M, N, K):
     # the path (rotation + linear) captured once in a graph; every replay,
