@@ -45,7 +45,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 PEAK_VALU_DOT4_TOPS = 256 * 4 * 16 * 2.4e9 * 8 / 1e12
 CACHE_BUST_BYTES = int(1.1e9)
 COPY_BYTES = 1 << 30
-SECTIONS = ("headline", "down", "decode", "stack")
+SECTIONS = ("headline", "down", "decode", "stack", "peaks")
 
 
 def log(msg: str) -> None:
@@ -422,6 +422,82 @@ def section_stack(torch, twl, steps, warmup):
     return out
 
 
+def section_peaks(torch):
+    """Measured peaks of this part, from the microbenchmark kernels of
+    libtwl_peaks.so, timed with HIP events on the stream they run on: the
+    int8 MFMA rate (the GEMM's instruction with no memory traffic), the HBM
+    read rate (nontemporal stream of 1 GiB), the time of one streaming read of
+    the decode weight size (22.3 MB, graph-captured back to back like the
+    decode calls), and the VALU v_dot4 int8 rate."""
+    import ctypes
+    from ternary_weight_linear_block_amd.build import PEAKS_LIB_PATH
+    if not os.path.exists(PEAKS_LIB_PATH):
+        raise ImportError(f"{PEAKS_LIB_PATH} is missing: build it first "
+                          "(python -m ternary_weight_linear_block_amd.build)")
+    lib = ctypes.CDLL(PEAKS_LIB_PATH)
+    P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.twl_peak_mfma_i8.argtypes = [I, I, P, P]
+    lib.twl_peak_read.argtypes = [P, S, I, P, P]
+    lib.twl_peak_dot4.argtypes = [I, I, P, P]
+    for f in (lib.twl_peak_mfma_i8, lib.twl_peak_read, lib.twl_peak_dot4):
+        f.restype = I
+    sink = torch.zeros(16, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: HIP error {rc}")
+
+    wgs, iters = 1024, 2000
+    ms = timed(lambda: check(lib.twl_peak_mfma_i8(wgs, iters, sink.data_ptr(), h), "mfma peak"))
+    mfma_tops = 2.0 * 32 * 32 * 32 * 10 * iters * wgs * 4 / (ms * 1e-3) / 1e12
+    ms = timed(lambda: check(lib.twl_peak_dot4(wgs, iters, sink.data_ptr(), h), "dot4 peak"))
+    dot4_tops = 8.0 * 8 * iters * wgs * 256 / (ms * 1e-3) / 1e12
+    big = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    big.fill_(1)
+    ms = timed(lambda: check(lib.twl_peak_read(big.data_ptr(), COPY_BYTES, 8192, sink.data_ptr(), h),
+                             "read peak"))
+    read_gbs = COPY_BYTES / (ms * 1e-3) / 1e9
+    # one decode-sized read per launch, 48 launches over distinct buffers
+    wb = weight_bytes(17408, 5120) // 16 * 16
+    copies = 48
+    step = (wb + 4095) // 4096 * 4096
+    pool = torch.empty(step * copies, dtype=torch.uint8, device="cuda")
+    pool.fill_(1)
+    it = [0]
+
+    def one():
+        # on the stream current at call time: graph_time_ms captures on its own
+        k = it[0] % copies
+        it[0] += 1
+        check(lib.twl_peak_read(pool.data_ptr() + k * step, wb, 2048, sink.data_ptr(),
+                                torch.cuda.current_stream().cuda_stream), "read call")
+
+    call_ms = graph_time_ms(torch, one, copies)
+    del big, pool
+    torch.cuda.empty_cache()
+    return {"int8_mfma_tops": round(mfma_tops, 1), "int8_mfma_frac_of_spec": round(mfma_tops / PEAK_INT8_TOPS, 4),
+            "hbm_read_gbs": round(read_gbs, 1), "hbm_read_frac_of_spec": round(read_gbs / PEAK_HBM_GBS, 4),
+            "decode_size_read_us": round(call_ms * 1e3, 2), "decode_size_read_bytes": wb,
+            "valu_dot4_tops": round(dot4_tops, 1)}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description="ternary linear layer benchmark (one MI355X)")
     ap.add_argument("--gpus", type=int, default=1)
@@ -464,6 +540,11 @@ def main(argv=None) -> int:
     if "stack" in sections:
         log("64-layer stack")
         detail["stack"] = section_stack(torch, twl, max(2, args.steps // 10), 1)
+    peaks = None
+    if "peaks" in sections:
+        log("measured peaks (microbenchmarks)")
+        peaks = section_peaks(torch)
+        detail["measured_peaks"] = peaks
 
     ops = 2.0 * layer.M * layer.N * layer.K
     achieved = ops / head["linear_ms"] / 1e9
@@ -472,6 +553,9 @@ def main(argv=None) -> int:
                 "traffic": traffic_for("gemm_i8.hip", "prefill_gate_up"),
                 "kernel": "gemm_kernel (ternary_linear GEMM path)",
                 "algorithmic_ops_per_launch": ops}
+    if peaks:
+        roofline["measured_peak"] = peaks["int8_mfma_tops"]
+        roofline["frac_of_measured_peak"] = round(achieved / peaks["int8_mfma_tops"], 4)
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")

@@ -22,6 +22,10 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libtwl.so")
+# microbenchmark kernels for the measured peaks bench.py reports (not part of
+# the library's C ABI)
+PEAKS_SRC = "peaks.hip"
+PEAKS_LIB_PATH = os.path.join(PKG_DIR, "libtwl_peaks.so")
 
 SOURCES = ["rotate_quant.hip", "pack.hip", "gemm_i8.hip", "gemv.hip", "reference_bf16.hip", "api.cpp"]
 
@@ -69,20 +73,27 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(jobs: int = 0, verbose: bool = False) -> str:
-    """Compile every source and link libtwl.so; returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 8)
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str, verbose: bool) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"linking libtwl.so failed:\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+        raise RuntimeError(f"linking {os.path.basename(path)} failed:\n{res.stdout}{res.stderr}")
+    os.replace(tmp, path)
+
+
+def build(jobs: int = 0, verbose: bool = False) -> str:
+    """Compile every source, link libtwl.so (and the peaks microbenchmark
+    library libtwl_peaks.so); returns the libtwl.so path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + [PEAKS_SRC]
+    jobs = jobs or min(len(srcs), os.cpu_count() or 1, 8)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:len(SOURCES)], LIB_PATH, verbose)
+    _link(objs[len(SOURCES):], PEAKS_LIB_PATH, verbose)
     return LIB_PATH
 
 

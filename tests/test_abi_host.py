@@ -104,3 +104,14 @@ def test_empty_shapes_enqueue_nothing(lib):
     assert lib.twl_ternary_linear(None, None, None, None, None, 0, 5, 1024, None, None, 0, None) == 0
     assert lib.twl_ternary_linear(None, None, None, None, None, 5, 0, 1024, None, None, 0, None) == 0
     assert lib.twl_last_error() == b""
+
+
+def test_peaks_library_exports_its_microbenchmarks():
+    # libtwl_peaks.so: the microbenchmark kernels bench.py times for the
+    # measured peaks (not part of the ternary-linear ABI); loading only
+    from ternary_weight_linear_block_amd.build import PEAKS_LIB_PATH
+    if not os.path.exists(PEAKS_LIB_PATH):
+        pytest.skip("libtwl_peaks.so not built")
+    lib = ctypes.CDLL(PEAKS_LIB_PATH)
+    for name in ("twl_peak_mfma_i8", "twl_peak_read", "twl_peak_dot4"):
+        assert hasattr(lib, name), name
