@@ -267,7 +267,19 @@ def cpu_baseline(layer, min_s=12.0, max_reps=400):
     return {"value": round(ops / el / 1e12, 4), "unit": "TOPS", "cores": int(threads), "kind": "oracle",
             "sample": f"{reps} full steps (rotate_quant_act + ternary_linear, M={layer.M} K={layer.K} "
                       f"N={layer.N}) in {el:.1f} s; numpy, BLAS threads={threads}, "
-                      f"affine cores={len(os.sched_getaffinity(0))}"}
+                      f"affine cores={len(os.sched_getaffinity(0))}, cpu={cpu_model()}"}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo (empty if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
 
 
 def copy_calibration(torch) -> int:
