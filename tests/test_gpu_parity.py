@@ -207,6 +207,49 @@ def test_gemv_k_split_across_workgroups(twl, M, N, K, path):
         assert np.array_equal(acc2, oacc), f"rep {rep}: GEMM acc differs"
 
 
+def _extreme_operands(M, N, K, seed):
+    """x_i8 rows of +127, -127 or random; code rows of +1, -1 or random; all
+    scales equal, so q = 127 everywhere and acc reaches +-127*127*K."""
+    rng = np.random.default_rng(seed)
+    x_i8 = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    x_i8[0::3] = 127
+    x_i8[1::3] = -127
+    code = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    code[0::3] = 1
+    code[1::3] = -1
+    s_bits = np.full((N, K // 128), 0.02, dtype=np.float16).view(np.uint16)
+    a_scale = rng.uniform(0.5, 2.0, M).astype(np.float32)
+    return x_i8, a_scale, code, s_bits
+
+
+@pytest.mark.parametrize("M,N,K,paths", [
+    # the GEMM at the largest K the library takes (split over K)
+    (300, 130, 65536, ("gemm",)),
+    # the dot4 and K-split matrix-core decode kernels at the largest K
+    (1, 130, 65536, ("dot4", "mfma")),
+    (24, 130, 65536, ("dot4", "mfma")),
+    # the row-balanced decode kernel (>= 16 rows per CU) at its largest K:
+    # 8 waves x 33 groups of 128
+    (24, 4096, 33792, ("gemv", "gemm")),
+])
+def test_extreme_accumulators_at_max_k(twl, M, N, K, paths):
+    x_i8, a_scale, code, s_bits = _extreme_operands(M, N, K, 4000 + M + N)
+    packed, q, smax, oq, osm = _check_pack(twl, code, s_bits, f"extreme K={K}")
+    assert (oq == 127).all()
+    oacc = O.linear_acc(x_i8, code, oq)
+    # the oracle itself at the closed form: +-127*127*K where both rows are
+    # constant (same sign -> +, opposite -> -)
+    big = 127 * 127 * K
+    assert big < 2 ** 31
+    assert (oacc[0::3, 0::3] == big).all() and (oacc[1::3, 1::3] == big).all()
+    assert (oacc[0::3, 1::3] == -big).all() and (oacc[1::3, 0::3] == -big).all()
+    ids = {"gemm": twl.PATH_GEMM, "gemv": twl.PATH_GEMV, "dot4": twl.PATH_GEMV_DOT4,
+           "mfma": twl.PATH_GEMV_MFMA}
+    for name in paths:
+        _check_linear(twl, x_i8, a_scale, packed, q, smax, code, oq, osm, ids[name],
+                      f"extreme {name} M={M}")
+
+
 def test_rotate_edge_cases(twl):
     # maximum width (64 blocks), one token
     layer = W.make_layer(31, 2, 65536, 1)
