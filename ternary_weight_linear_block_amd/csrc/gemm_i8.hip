@@ -46,8 +46,9 @@
 //     stage.  No load into VGPRs happens inside the loop, so the compiler
 //     never has to drain vmcnt.
 //   * Optional split-K over stages: each split stores its exact int32 partial
-//     tile (lane-major, fully coalesced) to a workspace slot and a second,
-//     small kernel adds the splits and runs the epilogue.  (A device-scope
+//     tile (lane-major, fully coalesced) to a workspace slot and a second
+//     kernel, one wave per output fragment, adds the splits and runs the
+//     epilogue.  (A device-scope
 //     fence + counter scheme in one kernel was measured to cost far more: on
 //     this multi-XCD part each fence writes back the L2.)
 //   * Tiles are ordered so that the workgroups sharing a column block (the
@@ -234,85 +235,69 @@ __device__ __forceinline__ void lds_wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Only the fragments i * RN + j in [f_lo, f_hi) are written (the wave pair
-// splits the tile's fragments between its two waves).
-template <int RM, int FN, int OUT>
-__device__ __forceinline__ void store_tile(const v16i (&acc)[RM][(FN + 1) / 2], void* out,
-                                           const float* row_scale, const float* col_scale,
-                                           int M, int N, int m0, int n0, int wm, int wn,
-                                           int lane, int32_t* tr, int f_lo, int f_hi) {
-  constexpr int RN = (FN + 1) / 2;
+// Stores one 32x32 fragment of one wave (MFMA layout: lane l32 = column,
+// register r = row 8 (r / 4) + 4 (lane / 32) + r % 4) with its epilogue.
+// row0/col0: the fragment's first output row and column; rs/cs: the scales of
+// its 32 rows and 32 columns.  With N % 4 == 0 it goes through the wave's LDS
+// transpose buffer tr and leaves as 16-byte stores of 4 columns (8 for bf16
+// when N % 8 == 0); otherwise element by element.  Rows past M and columns
+// past N are not stored.
+template <int OUT>
+__device__ __forceinline__ void store_frag(const v16i& acc, void* out, const float* rs, const float* cs,
+                                           int M, int N, int row0, int col0, int lane, int32_t* tr) {
   const int l32 = lane & 31, half = lane >> 5;
-  const bool vec = (N & 3) == 0;
+  const float cscale = OUT == kOutAcc ? 0.0f : cs[l32] * (1.0f / 127.0f);
+  if ((N & 3) != 0) {
+    const int col = col0 + l32;
+    if (col >= N) return;
 #pragma unroll
-  for (int j = 0; j < RN; ++j) {
-    const int f = wn * RN + j;
-    if (f >= FN) continue;  // padding fragment
-    const int cl = 32 * f + l32;
-    const int col = n0 + cl;
-    if (!vec && col >= N) continue;
-    const float cscale = OUT == kOutAcc ? 0.0f : col_scale[cl] * (1.0f / 127.0f);
+    for (int r = 0; r < 16; ++r) {
+      const int rr = 8 * (r >> 2) + 4 * half + (r & 3);
+      if (row0 + rr < M)
+        store_out(out, static_cast<size_t>(row0 + rr) * N + col, OUT, acc[r],
+                  OUT == kOutAcc ? 0.0f : static_cast<float>(acc[r]) * rs[rr] * cscale);
+    }
+    return;
+  }
 #pragma unroll
-    for (int i = 0; i < RM; ++i) {
-      if (i * RN + j < f_lo || i * RN + j >= f_hi) continue;
-      const int rbase = wm * 32 * RM + 32 * i;  // first row of the fragment in the tile
-      if (!vec) {
+  for (int r = 0; r < 16; ++r) {
+    const int rr = 8 * (r >> 2) + 4 * half + (r & 3);
+    tr[rr * kTrStride + l32] =
+        OUT == kOutAcc ? acc[r] : __float_as_int(static_cast<float>(acc[r]) * rs[rr] * cscale);
+  }
+  lds_wave_sync();
+  if (OUT == kOutBf16 && (N & 7) == 0) {
+    // 8 columns per lane: one 16-byte store covers 16 rows of the fragment
+    const int c8 = 8 * (lane & 3);
+    const int gcol = col0 + c8;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rl = rbase + 8 * (r >> 2) + 4 * half + (r & 3);
-          const int row = m0 + rl;
-          if (row < M) {
-            const size_t o = static_cast<size_t>(row) * N + col;
-            const float v = OUT == kOutAcc ? 0.0f : static_cast<float>(acc[i][j][r]) * row_scale[rl] * cscale;
-            store_out(out, o, OUT, acc[i][j][r], v);
-          }
-        }
-        continue;
+    for (int k = 0; k < 2; ++k) {
+      const int rr = 16 * k + (lane >> 2);
+      const v4i a = *reinterpret_cast<const v4i*>(tr + rr * kTrStride + c8);
+      const v4i b = *reinterpret_cast<const v4i*>(tr + rr * kTrStride + c8 + 4);
+      const int grow = row0 + rr;
+      if (grow < M && gcol < N) {  // N % 8 == 0: all eight columns are in range
+        const uint4 w = make_uint4(bf16_pair(a.x, a.y), bf16_pair(a.z, a.w), bf16_pair(b.x, b.y),
+                                   bf16_pair(b.z, b.w));
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + static_cast<size_t>(grow) * N + gcol) = w;
       }
-      lds_wave_sync();  // the previous fragment's reads are done
+    }
+    return;
+  }
+  const int c4 = 4 * (lane & 7);
+  const int gcol = col0 + c4;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = 8 * (r >> 2) + 4 * half + (r & 3);
-        const int bits = OUT == kOutAcc
-                             ? acc[i][j][r]
-                             : __float_as_int(static_cast<float>(acc[i][j][r]) * row_scale[rbase + rr] * cscale);
-        tr[rr * kTrStride + l32] = bits;
-      }
-      lds_wave_sync();
-      if (OUT == kOutBf16 && (N & 7) == 0) {
-        // 8 columns per lane: one 16-byte store covers 16 rows of the fragment
-        const int c8 = 8 * (lane & 3);
-        const int gcol = n0 + 32 * f + c8;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int rr = 16 * k + (lane >> 2);
-          const v4i a = *reinterpret_cast<const v4i*>(tr + rr * kTrStride + c8);
-          const v4i b = *reinterpret_cast<const v4i*>(tr + rr * kTrStride + c8 + 4);
-          const int grow = m0 + rbase + rr;
-          if (grow < M && gcol < N) {  // N % 8 == 0: all eight columns are in range
-            const uint4 w = make_uint4(bf16_pair(a.x, a.y), bf16_pair(a.z, a.w), bf16_pair(b.x, b.y),
-                                       bf16_pair(b.z, b.w));
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + static_cast<size_t>(grow) * N + gcol) = w;
-          }
-        }
-        continue;
-      }
-      const int c4 = 4 * (lane & 7);
-      const int gcol = n0 + 32 * f + c4;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int rr = 8 * k + (lane >> 3);
-        const v4i v = *reinterpret_cast<const v4i*>(tr + rr * kTrStride + c4);
-        const int grow = m0 + rbase + rr;
-        if (grow < M && gcol < N) {  // N % 4 == 0: all four columns are in range
-          const size_t o = static_cast<size_t>(grow) * N + gcol;
-          if (OUT == kOutBf16)
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) =
-                make_uint2(bf16_pair(v.x, v.y), bf16_pair(v.z, v.w));
-          else
-            *reinterpret_cast<v4i*>(static_cast<int32_t*>(out) + o) = v;
-        }
-      }
+  for (int k = 0; k < 4; ++k) {
+    const int rr = 8 * k + (lane >> 3);
+    const v4i v = *reinterpret_cast<const v4i*>(tr + rr * kTrStride + c4);
+    const int grow = row0 + rr;
+    if (grow < M && gcol < N) {  // N % 4 == 0: all four columns are in range
+      const size_t o = static_cast<size_t>(grow) * N + gcol;
+      if (OUT == kOutBf16)
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) =
+            make_uint2(bf16_pair(v.x, v.y), bf16_pair(v.z, v.w));
+      else
+        *reinterpret_cast<v4i*>(static_cast<int32_t*>(out) + o) = v;
     }
   }
 }
@@ -755,48 +740,61 @@ __global__ __launch_bounds__(64 * 2 * WN * WK, 1) void gemm_kernel(GemmArgs p) {
   finish_tile<RM, FN, WK, WN, OUT>(acc, p, w, smem, row_scale, col_scale, wave, wk, lane);
 }
 
-// Split-K second pass: one workgroup per block tile, four waves in the same
-// (wm, wn) roles as the GEMM's wk = 0 waves; adds the splits' partial tiles
-// (exact int32) and runs the same epilogue.
+// Split-K second pass: one wave per output fragment (block tile, wave role
+// (wm, wn) of the GEMM's wk = 0 waves, fragment i * RN + j), so that the
+// partial tiles are read by a grid that spans the chip; adds the splits'
+// partial fragments in split order (exact int32) and runs the same epilogue.
 template <int RM, int FN, int OUT>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p) {
+__global__ __launch_bounds__(64) void splitk_reduce_kernel(GemmArgs p) {
   using T = Tile<RM, FN, 1>;
-  constexpr int RN = T::RN;
-  __shared__ float row_scale[T::BM];
-  __shared__ float col_scale[T::BN];
-  __shared__ __attribute__((aligned(16))) int32_t tr_lds[4][32 * kTrStride];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tile = blockIdx.x;
+  constexpr int RN = T::RN, NF = RM * RN, NP = 4;  // NP: wave roles (wm, wn)
+  __shared__ float scales[64];  // the fragment's 32 row scales, then its 32 column scales
+  __shared__ __attribute__((aligned(16))) int32_t tr_lds[32 * kTrStride];
+  const int lane = threadIdx.x;
+  const int unit = blockIdx.x;
+  const int q = unit % NF, pair = (unit / NF) % NP, tile = unit / (NF * NP);
+  const int i = q / RN, j = q % RN, wm = pair & 1, wn = pair >> 1;
+  const int f = wn * RN + j;  // column fragment within the tile
+  if (f >= FN) return;        // padding fragment: nothing to store
   const int m0 = (tile % p.tiles_m) * T::BM, n0 = (tile / p.tiles_m) * p.tile_sn;
+  const int row0 = m0 + wm * 32 * RM + 32 * i, col0 = n0 + 32 * f;
+  // one scale per lane (lanes 0-31: rows, 32-63: columns), loaded branch-free
+  // ahead of the partials and written to LDS after them
+  float sv = 0.0f;
   if (OUT != kOutAcc) {
-    for (int r = tid; r < T::BM; r += 256) row_scale[r] = p.a_scale[min(m0 + r, p.M - 1)];
-    for (int c = tid; c < T::BN; c += 256) col_scale[c] = p.smax[min(n0 + c, p.N - 1)];
+    const float rsv = p.a_scale[min(row0 + (lane & 31), p.M - 1)];
+    const float csv = p.smax[min(col0 + (lane & 31), p.N - 1)];
+    sv = lane < 32 ? rsv : csv;
   }
-  v16i acc[RM][RN];
+  v16i acc = v16i{0};
+  const int32_t* part = p.ws_part + static_cast<size_t>(tile) * p.splits * T::SLOT_INTS +
+                        (static_cast<size_t>((pair * RM + i) * RN + j) * 256 + lane) * 4;
+  // four splits' loads in flight at a time; a split index past the last is
+  // clamped to it (an in-bounds re-read) and its values are not added
+  for (int sp = 0; sp < p.splits; sp += 4) {
+    v4i v[4][4];
 #pragma unroll
-  for (int i = 0; i < RM; ++i)
+    for (int u = 0; u < 4; ++u) {
+      const int su = min(sp + u, p.splits - 1);
 #pragma unroll
-    for (int j = 0; j < RN; ++j) acc[i][j] = v16i{0};
-  const int32_t* part = p.ws_part + static_cast<size_t>(tile) * p.splits * T::SLOT_INTS;
-  for (int sp = 0; sp < p.splits; ++sp) {
+      for (int c = 0; c < 4; ++c)
+        v[u][c] = *reinterpret_cast<const v4i*>(part + static_cast<size_t>(su) * T::SLOT_INTS + c * 256);
+    }
 #pragma unroll
-    for (int i = 0; i < RM; ++i)
+    for (int u = 0; u < 4; ++u) {
+      const bool use = sp + u < p.splits;
 #pragma unroll
-      for (int j = 0; j < RN; ++j)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const v4i v = *reinterpret_cast<const v4i*>(
-              part + static_cast<size_t>(sp) * T::SLOT_INTS + ((((wave * RM + i) * RN + j) * 4 + c) * 64 + lane) * 4);
-          acc[i][j][4 * c] += v.x;
-          acc[i][j][4 * c + 1] += v.y;
-          acc[i][j][4 * c + 2] += v.z;
-          acc[i][j][4 * c + 3] += v.w;
-        }
+      for (int c = 0; c < 4; ++c) {
+        acc[4 * c] += use ? v[u][c].x : 0;
+        acc[4 * c + 1] += use ? v[u][c].y : 0;
+        acc[4 * c + 2] += use ? v[u][c].z : 0;
+        acc[4 * c + 3] += use ? v[u][c].w : 0;
+      }
+    }
   }
+  scales[lane] = sv;
   __syncthreads();
-  store_tile<RM, FN, OUT>(acc, p.out, row_scale, col_scale, p.M, p.N, m0, n0, wave & 1,
-                          wave >> 1, lane, tr_lds[wave], 0, RM * RN);
+  store_frag<OUT>(acc, p.out, scales, scales + 32, p.M, p.N, row0, col0, lane, tr_lds);
 }
 
 // ---------------------------------------------------------------- planner
@@ -906,7 +904,8 @@ hipError_t launch_cfg_out(const GemmArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits <= 1) return e;
   if (WN != 2) return hipErrorInvalidConfiguration;  // split-K is planned for WN = 2 only
-  hipLaunchKernelGGL((splitk_reduce_kernel<RM, FN, OUT>), dim3(tiles), dim3(256), 0, stream, a);
+  const unsigned units = tiles * 4u * static_cast<unsigned>(RM * T::RN);  // one wave per fragment
+  hipLaunchKernelGGL((splitk_reduce_kernel<RM, FN, OUT>), dim3(units), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
