@@ -250,6 +250,23 @@ def test_extreme_accumulators_at_max_k(twl, M, N, K, paths):
                       f"extreme {name} M={M}")
 
 
+@pytest.mark.parametrize("N", [5536, 5534])
+def test_gemm_split_k_with_padding_fragments(twl, N):
+    # a 128 x 288 tile (nine column fragments over two column waves, so one
+    # wave role holds a padding fragment) with three splits: the split-K
+    # reduce skips the padding fragment and stores the ragged last tile
+    # (N = 5536: 16-byte stores; N = 5534: element stores)
+    M, K = 512, 17408
+    rng = np.random.default_rng(5000 + N)
+    x_i8 = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    a_scale = rng.uniform(0.01, 0.1, M).astype(np.float32)
+    code = rng.choice(np.array([-1, 0, 1], dtype=np.int8), size=(N, K), p=[0.3, 0.4, 0.3])
+    s_bits = np.exp(rng.normal(-4, 0.5, (N, K // 128))).astype(np.float16).view(np.uint16)
+    packed, q, smax, oq, osm = _check_pack(twl, code, s_bits, f"split-K padding N={N}")
+    _check_linear(twl, x_i8, a_scale, packed, q, smax, code, oq, osm, twl.PATH_GEMM,
+                  f"split-K padding {M}x{N}x{K}")
+
+
 def test_rotate_edge_cases(twl):
     # maximum width (64 blocks), one token
     layer = W.make_layer(31, 2, 65536, 1)
