@@ -725,11 +725,14 @@ template <int NS, int MAXT>
 hipError_t launch_rows_ns(GemvArgs a, int M, const GemvPlan& pl, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(pl.rows_wgs));
   const dim3 block(64 * pl.nw);
-  // groups of loads in flight per wave, within the register budget
+  // groups of loads in flight per wave, within the register budget.  With 5
+  // groups per wave (K = 5120) two in flight leave the workgroup 65 KB of LDS
+  // and 123 VGPRs, so two workgroups share a CU (measured 4-18% faster than
+  // five in flight, most where N needs two rounds of workgroups).
   constexpr int PM = 5;
   switch (pl.gmax) {
     case 3: hipLaunchKernelGGL((gemv_rows_kernel<NS, 3, 3, MAXT>), grid, block, 0, stream, a, M); break;
-    case 5: hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, PM, MAXT>), grid, block, 0, stream, a, M); break;
+    case 5: hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 2, MAXT>), grid, block, 0, stream, a, M); break;
     case 9: hipLaunchKernelGGL((gemv_rows_kernel<NS, 9, PM, MAXT>), grid, block, 0, stream, a, M); break;
     case 17: hipLaunchKernelGGL((gemv_rows_kernel<NS, 17, PM, MAXT>), grid, block, 0, stream, a, M); break;
     case 33: hipLaunchKernelGGL((gemv_rows_kernel<NS, 33, PM, MAXT>), grid, block, 0, stream, a, M); break;
