@@ -525,7 +525,7 @@ def main(argv=None) -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only (no collectives, no sharding); "
+        print("bench.py: this library runs on one GPU only (no collectives, no sharding); "
               "run it with --gpus 1", file=sys.stderr)
         return 2
 
