@@ -219,6 +219,26 @@ twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const
                                  void* out, int out_kind, int path,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * plan_info -- the kernels twl_ternary_linear_ex would launch for this shape
+ * and path on the current device, without launching anything (for tests and
+ * tuning; the choice is a function of M, N, K, path and the CU count only).
+ * Writes eight values to info (host memory, caller-owned):
+ *   info[0] kernel family: 1 = prefill GEMM, 2 = row-balanced MFMA decode,
+ *           3 = dot4 decode, 4 = K-split MFMA decode
+ *   info[1] GEMM block-tile rows, or (decode) rows per workgroup at most
+ *   info[2] GEMM block-tile columns (0 for decode)
+ *   info[3] K splits: GEMM split-K count or decode K slices (1 = not split)
+ *   info[4] workgroups of the main kernel
+ *   info[5] waves per workgroup
+ *   info[6] 1 when a second (reduce) kernel follows, else 0
+ *   info[7] workspace bytes this path needs
+ * M = 0 or N = 0 writes zeros.  Errors as twl_ternary_linear_ex (shape, path,
+ * decode batch limit), TWL_EINVAL for a NULL info, TWL_EDEVICE / TWL_EHIP
+ * when the current device is not a usable gfx950.
+ */
+twl_status twl_plan_info(int64_t M, int64_t N, int64_t K, int path, int64_t* info);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* twl_last_error(void);
 

@@ -22,7 +22,7 @@ from ._lib import (GEMV_MAX_M, GROUP, HBLOCK, MAX_K, PATH_AUTO, PATH_GEMM, PATH_
 __all__ = [
     "rotate_quant_act", "silu_mul_rotate_quant_act", "pack_ternary", "rotate_act_bf16",
     "reference_linear_bf16", "ternary_linear", "ternary_linear_acc", "ternary_linear_bf16",
-    "workspace_bytes", "packed_bytes", "TwlError", "PATH_AUTO", "PATH_GEMM", "PATH_GEMV", "PATH_GEMV_DOT4",
+    "workspace_bytes", "packed_bytes", "plan_info", "TwlError", "PATH_AUTO", "PATH_GEMM", "PATH_GEMV", "PATH_GEMV_DOT4",
     "PATH_GEMV_MFMA", "GEMV_MAX_M",
     "HBLOCK", "GROUP", "MAX_K", "library",
 ]
@@ -159,6 +159,41 @@ def workspace_bytes(M: int, N: int, K: int) -> int:
     return int(_lib.load().twl_workspace_bytes(M, N, K))
 
 
+def plan_info(M: int, N: int, K: int, path: int = PATH_AUTO) -> dict:
+    """The kernels ternary_linear would launch for this shape and path on the
+    current device (twl_plan_info): family, tile, K splits, workgroups, waves,
+    reduce kernel, workspace bytes."""
+    import ctypes
+    info = (ctypes.c_int64 * 8)()
+    st = _lib.load().twl_plan_info(M, N, K, path, ctypes.cast(info, ctypes.c_void_p))
+    _lib.check(st, "twl_plan_info")
+    family = {0: "none", 1: "gemm", 2: "decode_rows", 3: "decode_dot4", 4: "decode_mfma"}[info[0]]
+    keys = ("tile_rows", "tile_cols", "splits", "workgroups", "waves", "reduce_kernel", "workspace_bytes")
+    return {"family": family, **{k: int(v) for k, v in zip(keys, info[1:])}}
+
+
+# One workspace per (device, stream) for calls that pass none: grown on demand,
+# never cleared (the kernels need no initial contents), reused by every later
+# call on that stream, so the hot path does not allocate.  Calls on one stream
+# run in order, so sharing it there is safe.
+_WORKSPACES = {}
+
+
+def _default_workspace(need: int, device, stream_handle: int):
+    torch = _torch()
+    key = (device.index if device.index is not None else torch.cuda.current_device(), stream_handle)
+    ws = _WORKSPACES.get(key)
+    if ws is not None and ws.numel() >= need:
+        return ws
+    if torch.cuda.is_current_stream_capturing():
+        raise RuntimeError(
+            f"ternary_linear needs a {need}-byte workspace and none is cached for this stream; "
+            "pass workspace= (a uint8 tensor of workspace_bytes(M, N, K) bytes) when capturing a graph")
+    ws = torch.empty(need, dtype=torch.uint8, device=device)
+    _WORKSPACES[key] = ws
+    return ws
+
+
 def _linear(x_i8, a_scale, packed, q, smax, out_kind: int, path: int, out=None, workspace=None,
             stream=None):
     torch = _torch()
@@ -176,9 +211,10 @@ def _linear(x_i8, a_scale, packed, q, smax, out_kind: int, path: int, out=None, 
         out = torch.empty((M, N), dtype=out_dtype, device=x_i8.device)
     need = workspace_bytes(M, N, K)
     ws_ptr, ws_len = None, 0
+    stream_handle = _stream_handle(stream)
     if need:
         if workspace is None:
-            workspace = torch.zeros(need, dtype=torch.uint8, device=x_i8.device)
+            workspace = _default_workspace(need, x_i8.device, stream_handle)
         ws_ptr, ws_len = _dev_ptr(workspace, "workspace", (torch.uint8,)), workspace.numel()
     st = lib.twl_ternary_linear_ex(
         _dev_ptr(x_i8, "x_i8", (torch.int8,)),
@@ -186,7 +222,7 @@ def _linear(x_i8, a_scale, packed, q, smax, out_kind: int, path: int, out=None, 
         _dev_ptr(packed, "packed", (torch.uint8,)), _dev_ptr(q, "q", (torch.int8,)),
         None if out_acc else _dev_ptr(smax, "smax", (torch.float32,)),
         M, N, K, _dev_ptr(out, "out", (out_dtype,)),
-        out_kind, path, ws_ptr, ws_len, _stream_handle(stream))
+        out_kind, path, ws_ptr, ws_len, stream_handle)
     _lib.check(st, "twl_ternary_linear_ex")
     return out
 

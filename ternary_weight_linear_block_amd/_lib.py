@@ -35,6 +35,7 @@ SIGNATURES = [
     ("twl_ternary_linear_acc", _INT, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _SIZE, _P]),
     ("twl_ternary_linear_ex", _INT,
      [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _INT, _INT, _P, _SIZE, _P]),
+    ("twl_plan_info", _INT, [_I64, _I64, _I64, _INT, _P]),
     ("twl_last_error", ctypes.c_char_p, []),
     ("twl_abi_version", _INT, []),
 ]

@@ -250,6 +250,33 @@ twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const
                   "ternary_linear (GEMM)");
 }
 
+twl_status twl_plan_info(int64_t M, int64_t N, int64_t K, int path, int64_t* info) {
+  TWL_TRY(check_rows("M", M));
+  TWL_TRY(check_rows("N", N));
+  TWL_TRY(check_k(K));
+  if (path < TWL_PATH_AUTO || path > TWL_PATH_GEMV_MFMA)
+    return fail(TWL_EINVAL, "unknown path %d", path);
+  const bool decode_path = path >= TWL_PATH_GEMV;
+  if (decode_path && M > TWL_GEMV_MAX_M)
+    return fail(TWL_ESHAPE, "the decode paths take M <= %d (got %lld)", TWL_GEMV_MAX_M,
+                static_cast<long long>(M));
+  if (info == nullptr) return fail(TWL_EINVAL, "info is NULL");
+  for (int i = 0; i < 8; ++i) info[i] = 0;
+  if (M == 0 || N == 0) return ok();
+  twl::DeviceInfo dev;
+  TWL_TRY(current_device(&dev));
+  const bool use_gemv = decode_path || (path == TWL_PATH_AUTO && M <= TWL_GEMV_MAX_M);
+  if (use_gemv) {
+    const twl::GemvKind kind = path == TWL_PATH_GEMV_DOT4   ? twl::kGemvDot4
+                               : path == TWL_PATH_GEMV_MFMA ? twl::kGemvMfma
+                                                            : twl::kGemvAuto;
+    twl::gemv_plan_info(M, N, K, kind, dev, info);
+  } else {
+    twl::gemm_plan_info(M, N, K, dev, info);
+  }
+  return ok();
+}
+
 twl_status twl_ternary_linear(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
                               const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
                               float* y, void* workspace, size_t workspace_bytes,

@@ -920,6 +920,18 @@ hipError_t launch_cfg(const GemmArgs& a, OutKind out_kind, hipStream_t stream) {
 
 }  // namespace
 
+void gemm_plan_info(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, int64_t* info) {
+  const Plan pl = make_plan(M, N, K, std::max(1, dev.cu_count));
+  info[0] = 1;
+  info[1] = 64 * pl.rm;
+  info[2] = 32 * pl.fn;
+  info[3] = pl.splits;
+  info[4] = static_cast<int64_t>(pl.tiles_m) * pl.tiles_n * pl.splits;
+  info[5] = 2 * pl.wn * pl.wk;
+  info[6] = pl.splits > 1 ? 1 : 0;
+  info[7] = static_cast<int64_t>(plan_workspace_bytes(pl));
+}
+
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   return plan_workspace_bytes(make_plan(M, N, K, std::max(1, dev.cu_count)));

@@ -776,6 +776,19 @@ hipError_t launch_mt(GemvArgs a, const GemvPlan& pl, hipStream_t stream) {
 
 }  // namespace
 
+void gemv_plan_info(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceInfo& dev, int64_t* info) {
+  const GemvPlan pl = make_plan(M, N, K, kind, dev);
+  const bool rows = pl.rows_ns > 0;
+  info[0] = rows ? 2 : (pl.mfma ? 4 : 3);
+  info[1] = rows ? (N + pl.rows_wgs - 1) / pl.rows_wgs : 64;
+  info[2] = 0;
+  info[3] = pl.slices;
+  info[4] = rows ? pl.rows_wgs : static_cast<int64_t>(pl.n_rb) * pl.slices;
+  info[5] = pl.nw;
+  info[6] = pl.slices > 1 ? 1 : 0;
+  info[7] = pl.slices > 1 ? static_cast<int64_t>(pl.slices) * M * N * 4 : 0;
+}
+
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceInfo& dev) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   const GemvPlan pl = make_plan(M, N, K, kind, dev);

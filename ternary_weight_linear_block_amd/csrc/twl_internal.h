@@ -57,6 +57,8 @@ hipError_t launch_gemm(const int8_t* x_i8, const float* a_scale, const uint8_t* 
                        void* out, OutKind out_kind, void* workspace, size_t workspace_bytes,
                        const DeviceInfo& dev, hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev);
+// The GEMM plan for this shape, as twl_plan_info reports it (info[0..7]).
+void gemm_plan_info(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev, int64_t* info);
 
 // Decode kernels (M <= 24): kGemvAuto picks by M, kGemvDot4 / kGemvMfma force
 // one.  When K is split across workgroups (gemv_workspace_bytes > 0) the
@@ -67,5 +69,7 @@ hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* 
                        void* out, OutKind out_kind, void* part, size_t part_bytes, GemvKind kind,
                        const DeviceInfo& dev, hipStream_t stream);
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceInfo& dev);
+// The decode plan for this shape, as twl_plan_info reports it (info[0..7]).
+void gemv_plan_info(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceInfo& dev, int64_t* info);
 
 }  // namespace twl

@@ -1,13 +1,14 @@
 """Checks on the generated gfx950 code that need no GPU.
 
-The GEMM issues its direct global->LDS loads from inline asm that sets M0
-itself.  LLVM treats M0 as a reserved register and does not preserve it
-around inline asm, so the kernel is only correct while the compiler never uses
-M0 for anything else.  This test compiles the GEMM to assembly with the
-library's own flags and checks that every M0 write is one of ours (an
+The GEMM and the row-balanced decode kernel issue their direct global->LDS
+loads from inline asm that sets M0 itself.  LLVM treats M0 as a reserved
+register and does not preserve it around inline asm, so these kernels are only
+correct while the compiler never uses M0 for anything else.  This test
+compiles both sources to assembly with the library's own flags and checks, in
+every instantiation of those kernels, that every M0 write is one of ours (an
 s_mov_b32 from an SGPR followed by a global_load_lds) and that M0 is read by
-nothing else.  It also checks the main loop keeps a single vmcnt wait per
-pipeline stage and no accumulator copies.
+nothing else.  It also checks the GEMM's main loop keeps a single vmcnt wait
+per pipeline stage and no accumulator copies.
 """
 import os
 import re
@@ -18,34 +19,43 @@ import pytest
 
 from ternary_weight_linear_block_amd import build as B
 
-SRC = os.path.join(B.CSRC, "gemm_i8.hip")
+# source file -> (kernel whose instantiations set M0 from inline asm, the
+# least number of instantiations expected)
+M0_KERNELS = {"gemm_i8.hip": ("gemm_kernel", 10), "gemv.hip": ("gemv_rows_kernel", 15)}
 
 
-@pytest.fixture(scope="module")
-def asm(tmp_path_factory):
+def _compile_asm(tmp_path_factory, src):
     if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / "gemm.s"
+    out = tmp_path_factory.mktemp("asm") / (os.path.splitext(src)[0] + ".s")
     cmd = [B.hipcc()] + [f for f in B.COMMON_FLAGS if f != "-fPIC"] + [
-        "--cuda-device-only", "-S", SRC, "-o", str(out)]
+        "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", str(out)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     return out.read_text()
 
 
-def _kernels(asm_text):
-    """name -> body for each gemm_kernel instantiation."""
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    return _compile_asm(tmp_path_factory, "gemm_i8.hip")
+
+
+def _kernels(asm_text, kernel="gemm_kernel", least=10):
+    """name -> body for each instantiation of `kernel`."""
     out = {}
-    for m in re.finditer(r"^(_Z\S*gemm_kernel\S*):[^\n]*\n(.*?)^\.Lfunc_end", asm_text, re.S | re.M):
+    for m in re.finditer(r"^(_Z\S*" + kernel + r"I\S*):[^\n]*\n(.*?)^\.Lfunc_end", asm_text, re.S | re.M):
         out[m.group(1)] = m.group(2)
-    assert len(out) >= 10, f"expected every gemm_kernel instantiation, found {len(out)}"
+    assert len(out) >= least, f"expected every {kernel} instantiation, found {len(out)}"
     return out
 
 
-def test_m0_only_feeds_our_lds_loads(asm):
-    kernels = _kernels(asm)
-    assert kernels, "no gemm_kernel found in the assembly"
+@pytest.mark.parametrize("src", sorted(M0_KERNELS))
+def test_m0_only_feeds_our_lds_loads(tmp_path_factory, asm, src):
+    text = asm if src == "gemm_i8.hip" else _compile_asm(tmp_path_factory, src)
+    kernel, least = M0_KERNELS[src]
+    kernels = _kernels(text, kernel, least)
     for name, body in kernels.items():
+        assert "global_load_lds" in body, name
         lines = [ln.strip() for ln in body.splitlines() if ln.strip() and not ln.strip().startswith(";")]
         for i, ln in enumerate(lines):
             if "m0" not in ln:

@@ -365,6 +365,38 @@ def test_bf16_output(twl, M, N, K, path):
     assert np.all(np.abs(y16f.astype(np.float64) - oy) <= 2.0**-8 * np.abs(oy.astype(np.float64)))
 
 
+@pytest.mark.parametrize("name,M,N,K,path,store", [
+    # prefill gate/up in full: the GEMM's own epilogue (no split-K), N % 8 == 0:
+    # 16-byte bf16 stores
+    ("prefill_gate_up", 512, 17408, 5120, "auto", "bf16x8"),
+    # N % 8 == 4: 8-byte bf16 stores of four columns
+    ("ragged_n8", 300, 24580, 1024, "gemm", "bf16x4"),
+    # N % 4 != 0: element stores straight from the accumulators
+    ("ragged_n4", 24, 24577, 1024, "gemm", "element"),
+])
+def test_bf16_output_gemm_epilogue_without_split(twl, name, M, N, K, path, store):
+    # bf16 y written by the GEMM's own store path (not the split-K reduce):
+    # the plan must not split K, so the tile's epilogue rounds and stores
+    p = {"auto": twl.PATH_AUTO, "gemm": twl.PATH_GEMM}[path]
+    plan = twl.plan_info(M, N, K, p)
+    assert plan["family"] == "gemm" and plan["splits"] == 1 and plan["reduce_kernel"] == 0, plan
+    if name == "prefill_gate_up":
+        layer = W.make_config(name)
+    else:
+        layer = W.make_layer(8000 + M + N, M, K, N, codes="sparse40")
+    x_i8, a_scale = O.rotate_quant_act(layer.x_bits, layer.sign)
+    packed, q, smax, oq, osm = _check_pack(twl, layer.code, layer.s_bits, f"bf16 {name}")
+    oy = O.epilogue(O.linear_acc(x_i8, layer.code, oq), a_scale, osm)
+    xi, sc = dev(x_i8), dev(a_scale)
+    announce(f"ternary_linear fp32 and bf16 {name} ({store}) M={M} N={N} K={K} plan={plan}")
+    y32 = host(twl.ternary_linear(xi, sc, packed, q, smax, path=p))
+    y16 = host(twl.ternary_linear_bf16(xi, sc, packed, q, smax, path=p).view(torch.int16)).view(np.uint16)
+    np.testing.assert_allclose(y32, oy, rtol=Y_RTOL, atol=0)
+    assert np.array_equal(y16, O.round_bf16(y32))
+    y16f = (y16.astype(np.uint32) << 16).view(np.float32)
+    assert np.all(np.abs(y16f.astype(np.float64) - oy) <= 2.0**-8 * np.abs(oy.astype(np.float64)))
+
+
 # ------------------------------- fused SiLU(gate) * up rotation (R13, R14)
 
 @pytest.mark.parametrize("M,K", [(256, 17408), (1, 17408), (24, 17408), (7, 5120), (3, 65536)])
@@ -470,3 +502,19 @@ def test_graph_replays_match_eager(twl, M, N, K):
     oy = O.ternary_linear(*O.rotate_quant_act(layer.x_bits, layer.sign), layer.code,
                           *O.decompose_scales(layer.s_bits))
     np.testing.assert_allclose(want_y, oy, rtol=Y_RTOL, atol=0)
+
+
+# ------------------------------------------------------------ plan queries
+
+@pytest.mark.parametrize("M,N,K,path,family", [
+    (512, 17408, 5120, 0, "gemm"), (256, 5120, 17408, 0, "gemm"),
+    (1, 17408, 5120, 0, "decode_rows"), (24, 5120, 17408, 0, "decode_rows"),
+    (2, 1000, 5120, 0, "decode_dot4"), (9, 200, 20480, 0, "decode_mfma"),
+    (24, 5120, 17408, 3, "decode_dot4"), (24, 5120, 17408, 1, "gemm")])
+def test_plan_info_matches_workspace_and_family(twl, M, N, K, path, family):
+    plan = twl.plan_info(M, N, K, path)
+    assert plan["family"] == family, plan
+    assert plan["splits"] >= 1 and plan["workgroups"] >= 1 and plan["waves"] >= 1
+    assert plan["reduce_kernel"] == (1 if plan["splits"] > 1 else 0)
+    assert plan["workspace_bytes"] <= twl.workspace_bytes(M, N, K)
+    assert (plan["workspace_bytes"] > 0) == (plan["splits"] > 1)

@@ -320,6 +320,34 @@ def test_epilogue_closed_form():
     assert np.array_equal(y, want)
 
 
+def test_epilogue_at_hand_values_and_full_epilogue():
+    # [P1] section 4's per-token (row) and per-weight-row (column) rescale,
+    # evaluated at listed (row, col) pairs.  Every row scale differs from every
+    # column scale, so reading a_scale by column or smax by row changes each
+    # value below (hand-worked: acc * a_scale[row] * smax[col] / 127).
+    a_scale = np.array([0.5, 2.0, 0.125, 8.0], dtype=np.float32)
+    smax = np.array([1.0, 0.25, 127.0, 4.0], dtype=np.float32)
+    rows = np.array([0, 1, 2, 3, 1, 2])
+    cols = np.array([2, 1, 3, 0, 0, 2])
+    acc = np.array([254, -127, 127, 127, 3, -8], dtype=np.int32)
+    want = np.array([127.0, -0.5, 0.5, 8.0, 6.0 / 127.0, -1.0], dtype=np.float64).astype(np.float32)
+    y = O.epilogue_at(acc, a_scale, smax, rows, cols)
+    assert y.dtype == np.float32
+    assert np.array_equal(y, want)
+    # the same scales read the other way round give other values
+    assert not np.array_equal(O.epilogue_at(acc, smax, a_scale, rows, cols), want)
+    # at sampled pairs of a full layer it equals the full epilogue bit for bit
+    layer = W.make_config("tiny")
+    x_i8, sc = O.rotate_quant_act(layer.x_bits, layer.sign)
+    q, sm = O.decompose_scales(layer.s_bits)
+    full = O.linear_acc(x_i8, layer.code, q)
+    rng = np.random.default_rng(11)
+    r = rng.integers(0, layer.M, 200)
+    c = rng.integers(0, layer.N, 200)
+    got = O.epilogue_at(full[r, c], sc, sm, r, c)
+    assert np.array_equal(got.view(np.uint32), O.epilogue(full, sc, sm)[r, c].view(np.uint32))
+
+
 # ----------------------------------------------------- end-to-end sanity ----
 
 def test_relative_error_vs_unquantised_is_about_1e2():
