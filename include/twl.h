@@ -220,6 +220,27 @@ twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * ternary_linear_noalloc -- for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same computation, kernels and results as
+ * twl_ternary_linear_ex (same arguments, same errors) without the workspace
+ * argument: K-split partial sums go to a scratch buffer the library owns, a
+ * static device array of TWL_NOALLOC_SCRATCH_BYTES on each GPU the library
+ * runs on (held until the process ends).  No call allocates or frees
+ * anything.  A shape whose plan needs more scratch than that returns
+ * TWL_ESHAPE (twl_workspace_bytes gives the need; use twl_ternary_linear_ex
+ * with a workspace for such shapes).  Every call on one GPU shares its
+ * scratch: calls that may overlap on one GPU (different streams, or
+ * different host threads) race and must be serialised by the caller.  The
+ * scratch needs no clearing: each call writes every partial sum it reads.
+ */
+#define TWL_NOALLOC_SCRATCH_BYTES (32u << 20)
+twl_status twl_ternary_linear_noalloc(const int8_t* x_i8, const float* a_scale,
+                                      const uint8_t* packed, const int8_t* q, const float* smax,
+                                      int64_t M, int64_t N, int64_t K, void* out, int out_kind,
+                                      int path, hipStream_t stream);
+
+/*
  * plan_info -- the kernels twl_ternary_linear_ex would launch for this shape
  * and path on the current device, without launching anything (for tests and
  * tuning; the choice is a function of M, N, K, path and the CU count only).

@@ -22,6 +22,7 @@ from ._lib import (GEMV_MAX_M, GROUP, HBLOCK, MAX_K, PATH_AUTO, PATH_GEMM, PATH_
 __all__ = [
     "rotate_quant_act", "silu_mul_rotate_quant_act", "pack_ternary", "rotate_act_bf16",
     "reference_linear_bf16", "ternary_linear", "ternary_linear_acc", "ternary_linear_bf16",
+    "ternary_linear_noalloc",
     "workspace_bytes", "packed_bytes", "plan_info", "TwlError", "PATH_AUTO", "PATH_GEMM", "PATH_GEMV", "PATH_GEMV_DOT4",
     "PATH_GEMV_MFMA", "GEMV_MAX_M",
     "HBLOCK", "GROUP", "MAX_K", "library",
@@ -224,6 +225,33 @@ def _linear(x_i8, a_scale, packed, q, smax, out_kind: int, path: int, out=None, 
         M, N, K, _dev_ptr(out, "out", (out_dtype,)),
         out_kind, path, ws_ptr, ws_len, stream_handle)
     _lib.check(st, "twl_ternary_linear_ex")
+    return out
+
+
+def ternary_linear_noalloc(x_i8, a_scale, packed, q, smax, out, path: int = PATH_AUTO, stream=None):
+    """The linear layer into a preallocated `out` (fp32 y, bf16 y or int32 acc,
+    by its dtype) through twl_ternary_linear_noalloc: K-split partial sums go
+    to the library's per-GPU scratch, so neither this call nor the library
+    allocates anything.  Calls that may overlap on one GPU must not be issued
+    concurrently (they share that scratch)."""
+    torch = _torch()
+    lib = _lib.load()
+    M, K = x_i8.shape
+    N = q.shape[0]
+    kinds = {torch.float32: _lib.OUT_F32, torch.int32: _lib.OUT_ACC_I32, torch.bfloat16: _lib.OUT_BF16}
+    if out.dtype not in kinds:
+        raise TypeError(f"out has dtype {out.dtype}, expected float32, bfloat16 or int32")
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(M, N)}")
+    out_kind = kinds[out.dtype]
+    out_acc = out_kind == _lib.OUT_ACC_I32
+    st = lib.twl_ternary_linear_noalloc(
+        _dev_ptr(x_i8, "x_i8", (torch.int8,)),
+        None if out_acc else _dev_ptr(a_scale, "a_scale", (torch.float32,)),
+        _dev_ptr(packed, "packed", (torch.uint8,)), _dev_ptr(q, "q", (torch.int8,)),
+        None if out_acc else _dev_ptr(smax, "smax", (torch.float32,)),
+        M, N, K, _dev_ptr(out, "out", (out.dtype,)), out_kind, path, _stream_handle(stream))
+    _lib.check(st, "twl_ternary_linear_noalloc")
     return out
 
 

@@ -17,6 +17,7 @@ STATUS_NAMES = {0: "TWL_OK", 1: "TWL_EINVAL", 2: "TWL_ESHAPE", 3: "TWL_EALIGN",
 PATH_AUTO, PATH_GEMM, PATH_GEMV, PATH_GEMV_DOT4, PATH_GEMV_MFMA = 0, 1, 2, 3, 4
 OUT_F32, OUT_ACC_I32, OUT_BF16 = 0, 1, 2
 HBLOCK, GROUP, MAX_K, GEMV_MAX_M = 1024, 128, 65536, 24
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # (name, restype, argtypes) for every symbol include/twl.h declares
 _P = ctypes.c_void_p
@@ -35,6 +36,8 @@ SIGNATURES = [
     ("twl_ternary_linear_acc", _INT, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _SIZE, _P]),
     ("twl_ternary_linear_ex", _INT,
      [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _INT, _INT, _P, _SIZE, _P]),
+    ("twl_ternary_linear_noalloc", _INT,
+     [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _INT, _INT, _P]),
     ("twl_plan_info", _INT, [_I64, _I64, _I64, _INT, _P]),
     ("twl_last_error", ctypes.c_char_p, []),
     ("twl_abi_version", _INT, []),

@@ -95,6 +95,97 @@ twl_status launched(hipError_t e, const char* what) {
   return ok();
 }
 
+// Library-owned K-split scratch for twl_ternary_linear_noalloc: one copy per
+// GPU, held until the process ends.  In host code `scratch` is only a stand-in
+// for the symbol; the device address of each GPU's copy comes from
+// hipGetSymbolAddress (called once per device, with that device current) and
+// is the only form ever passed to a kernel.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[TWL_NOALLOC_SCRATCH_BYTES];
+void* g_scratch_ptr[kMaxDevices];  // guarded by g_dev_mu
+
+// Device address of the current device's scratch (looked up on first use).
+twl_status current_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TWL_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TWL_EDEVICE, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(TWL_EHIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TWL_OK;
+}
+
+// The linear layer with the K-split partial sums either in the caller's
+// workspace or (use_scratch) in the library's per-device scratch.
+twl_status linear_impl(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
+                       const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
+                       void* out, int out_kind, int path, void* workspace, size_t workspace_bytes,
+                       bool use_scratch, hipStream_t stream) {
+  TWL_TRY(check_rows("M", M));
+  TWL_TRY(check_rows("N", N));
+  TWL_TRY(check_k(K));
+  if (path < TWL_PATH_AUTO || path > TWL_PATH_GEMV_MFMA)
+    return fail(TWL_EINVAL, "unknown path %d", path);
+  if (out_kind < TWL_OUT_F32 || out_kind > TWL_OUT_BF16)
+    return fail(TWL_EINVAL, "unknown output kind %d", out_kind);
+  const bool decode_path = path >= TWL_PATH_GEMV;
+  if (decode_path && M > TWL_GEMV_MAX_M)
+    return fail(TWL_ESHAPE, "the decode paths take M <= %d (got %lld)", TWL_GEMV_MAX_M,
+                static_cast<long long>(M));
+  if (M == 0 || N == 0) return ok();
+  TWL_REQUIRE_PTR(x_i8);
+  TWL_REQUIRE_PTR(packed);
+  TWL_REQUIRE_PTR(q);
+  TWL_REQUIRE_PTR(out);
+  if (out_kind != TWL_OUT_ACC_I32) {
+    TWL_REQUIRE_PTR(a_scale);
+    TWL_REQUIRE_PTR(smax);
+  }
+  twl::DeviceInfo dev;
+  TWL_TRY(current_device(&dev));
+  const bool use_gemv = decode_path || (path == TWL_PATH_AUTO && M <= TWL_GEMV_MAX_M);
+  const twl::GemvKind kind = path == TWL_PATH_GEMV_DOT4   ? twl::kGemvDot4
+                             : path == TWL_PATH_GEMV_MFMA ? twl::kGemvMfma
+                                                          : twl::kGemvAuto;
+  const size_t part = use_gemv ? twl::gemv_workspace_bytes(M, N, K, kind, dev)
+                               : twl::gemm_workspace_bytes(M, N, K, dev);
+  if (use_scratch) {
+    if (part > TWL_NOALLOC_SCRATCH_BYTES)
+      return fail(TWL_ESHAPE,
+                  "M=%lld N=%lld K=%lld needs %zu bytes of K-split scratch; the library's "
+                  "no-allocation scratch holds %zu (use twl_ternary_linear_ex with a workspace)",
+                  static_cast<long long>(M), static_cast<long long>(N), static_cast<long long>(K),
+                  part, static_cast<size_t>(TWL_NOALLOC_SCRATCH_BYTES));
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (part > 0) {
+      TWL_TRY(current_scratch(&workspace));
+      workspace_bytes = TWL_NOALLOC_SCRATCH_BYTES;
+    }
+  } else if (part > 0) {
+    if (workspace == nullptr || workspace_bytes < part)
+      return fail(TWL_EINVAL, "workspace of %zu bytes required (got %zu)", part,
+                  workspace == nullptr ? size_t{0} : workspace_bytes);
+    if (!aligned16(workspace)) return fail(TWL_EALIGN, "workspace is not 16-byte aligned");
+  }
+  if (use_gemv)
+    return launched(twl::launch_gemv(x_i8, a_scale, packed, q, smax, M, N, K, out,
+                                     static_cast<twl::OutKind>(out_kind), workspace,
+                                     workspace_bytes, kind, dev, stream),
+                    "ternary_linear (GEMV)");
+  return launched(twl::launch_gemm(x_i8, a_scale, packed, q, smax, M, N, K, out,
+                                   static_cast<twl::OutKind>(out_kind), workspace,
+                                   workspace_bytes, dev, stream),
+                  "ternary_linear (GEMM)");
+}
+
 }  // namespace
 
 extern "C" {
@@ -205,49 +296,16 @@ twl_status twl_ternary_linear_ex(const int8_t* x_i8, const float* a_scale, const
                                  const int8_t* q, const float* smax, int64_t M, int64_t N,
                                  int64_t K, void* out, int out_kind, int path, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
-  TWL_TRY(check_rows("M", M));
-  TWL_TRY(check_rows("N", N));
-  TWL_TRY(check_k(K));
-  if (path < TWL_PATH_AUTO || path > TWL_PATH_GEMV_MFMA)
-    return fail(TWL_EINVAL, "unknown path %d", path);
-  if (out_kind < TWL_OUT_F32 || out_kind > TWL_OUT_BF16)
-    return fail(TWL_EINVAL, "unknown output kind %d", out_kind);
-  const bool decode_path = path >= TWL_PATH_GEMV;
-  if (decode_path && M > TWL_GEMV_MAX_M)
-    return fail(TWL_ESHAPE, "the decode paths take M <= %d (got %lld)", TWL_GEMV_MAX_M,
-                static_cast<long long>(M));
-  if (M == 0 || N == 0) return ok();
-  TWL_REQUIRE_PTR(x_i8);
-  TWL_REQUIRE_PTR(packed);
-  TWL_REQUIRE_PTR(q);
-  TWL_REQUIRE_PTR(out);
-  if (out_kind != TWL_OUT_ACC_I32) {
-    TWL_REQUIRE_PTR(a_scale);
-    TWL_REQUIRE_PTR(smax);
-  }
-  twl::DeviceInfo dev;
-  TWL_TRY(current_device(&dev));
-  const bool use_gemv = decode_path || (path == TWL_PATH_AUTO && M <= TWL_GEMV_MAX_M);
-  const twl::GemvKind kind = path == TWL_PATH_GEMV_DOT4   ? twl::kGemvDot4
-                             : path == TWL_PATH_GEMV_MFMA ? twl::kGemvMfma
-                                                          : twl::kGemvAuto;
-  const size_t part = use_gemv ? twl::gemv_workspace_bytes(M, N, K, kind, dev)
-                               : twl::gemm_workspace_bytes(M, N, K, dev);
-  if (part > 0) {
-    if (workspace == nullptr || workspace_bytes < part)
-      return fail(TWL_EINVAL, "workspace of %zu bytes required (got %zu)", part,
-                  workspace == nullptr ? size_t{0} : workspace_bytes);
-    if (!aligned16(workspace)) return fail(TWL_EALIGN, "workspace is not 16-byte aligned");
-  }
-  if (use_gemv)
-    return launched(twl::launch_gemv(x_i8, a_scale, packed, q, smax, M, N, K, out,
-                                     static_cast<twl::OutKind>(out_kind), workspace,
-                                     workspace_bytes, kind, dev, stream),
-                    "ternary_linear (GEMV)");
-  return launched(twl::launch_gemm(x_i8, a_scale, packed, q, smax, M, N, K, out,
-                                   static_cast<twl::OutKind>(out_kind), workspace,
-                                   workspace_bytes, dev, stream),
-                  "ternary_linear (GEMM)");
+  return linear_impl(x_i8, a_scale, packed, q, smax, M, N, K, out, out_kind, path, workspace,
+                     workspace_bytes, false, stream);
+}
+
+twl_status twl_ternary_linear_noalloc(const int8_t* x_i8, const float* a_scale,
+                                      const uint8_t* packed, const int8_t* q, const float* smax,
+                                      int64_t M, int64_t N, int64_t K, void* out, int out_kind,
+                                      int path, hipStream_t stream) {
+  return linear_impl(x_i8, a_scale, packed, q, smax, M, N, K, out, out_kind, path, nullptr, 0,
+                     true, stream);
 }
 
 twl_status twl_plan_info(int64_t M, int64_t N, int64_t K, int path, int64_t* info) {

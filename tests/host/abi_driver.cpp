@@ -1,10 +1,10 @@
 // Host-only driver for the C ABI's validation and status mapping (api.cpp),
 // built with AddressSanitizer and UndefinedBehaviorSanitizer and run on the
 // CPU.  Nothing here touches a GPU: the few HIP runtime calls api.cpp makes
-// (hipGetDevice, hipGetDeviceProperties, hipGetErrorString) and the kernel
-// launchers it dispatches to are replaced by the stubs below, so a launch
-// failure, a wrong device or a failing runtime call can be forced from the
-// host and the returned status checked.
+// (hipGetDevice, hipGetDeviceProperties, hipGetErrorString,
+// hipGetSymbolAddress) and the kernel launchers it dispatches to are replaced
+// by the stubs below, so a launch failure, a wrong device or a failing
+// runtime call can be forced from the host and the returned status checked.
 //
 // Exit status 0 when every check passes; each failure prints one line.
 #include "twl.h"
@@ -40,6 +40,11 @@ size_t g_gemv_ws = 0;
 int64_t g_last_m = -1, g_last_n = -1, g_last_k = -1;
 int g_last_kind = -1;
 const void* g_last_ws = nullptr;
+// the no-allocation entry point's scratch lookup
+hipError_t g_symbol_status = hipSuccess;
+int g_symbol_lookups = 0;
+alignas(256) unsigned char g_fake_scratch_mem[256];
+void* g_fake_scratch = g_fake_scratch_mem;
 
 }  // namespace
 
@@ -59,6 +64,12 @@ hipError_t hipGetDeviceProperties(hipDeviceProp_t* prop, int dev) {
 }
 const char* hipGetErrorString(hipError_t e) {
   return e == hipSuccess ? "hipSuccess" : "stubbed HIP error";
+}
+hipError_t hipGetSymbolAddress(void** p, const void*) {
+  ++g_symbol_lookups;
+  if (g_symbol_status != hipSuccess) return g_symbol_status;
+  *p = g_fake_scratch;
+  return hipSuccess;
 }
 }
 
@@ -239,12 +250,63 @@ void test_dispatch_and_workspace() {
   CHECK(twl_plan_info(4, 8, 5000, TWL_PATH_AUTO, info) == TWL_ESHAPE);
 }
 
+void test_noalloc() {
+  auto* s8 = static_cast<const int8_t*>(P);
+  // no scratch needed: no lookup, no workspace passed
+  g_device = 2;
+  g_gemm_ws = g_gemv_ws = 0;
+  g_symbol_lookups = 0;
+  CHECK(twl_ternary_linear_noalloc(s8, (float*)P, (uint8_t*)P, s8, (float*)P, 64, 8, 1024, P, TWL_OUT_F32,
+                                   TWL_PATH_AUTO, nullptr) == TWL_OK);
+  CHECK(g_symbol_lookups == 0 && g_last_ws == nullptr && g_last_kind == 100 + twl::kOutF32);
+  // a failing symbol lookup maps to TWL_EHIP and launches nothing
+  g_gemm_ws = 4096;
+  g_symbol_status = hipErrorInvalidSymbol;
+  g_launches = 0;
+  CHECK(twl_ternary_linear_noalloc(s8, (float*)P, (uint8_t*)P, s8, (float*)P, 64, 8, 1024, P, TWL_OUT_F32,
+                                   TWL_PATH_AUTO, nullptr) == TWL_EHIP);
+  CHECK(msg_has("hipGetSymbolAddress") && g_launches == 0);
+  // then the scratch's device address is passed as the workspace; looked up
+  // once per device
+  g_symbol_status = hipSuccess;
+  g_symbol_lookups = 0;
+  for (int i = 0; i < 3; ++i) {
+    CHECK(twl_ternary_linear_noalloc(s8, (float*)P, (uint8_t*)P, s8, (float*)P, 64, 8, 1024, P,
+                                     TWL_OUT_ACC_I32, TWL_PATH_GEMM, nullptr) == TWL_OK);
+    CHECK(g_last_ws == g_fake_scratch && g_last_kind == 100 + twl::kOutAcc);
+  }
+  CHECK(g_symbol_lookups == 1);
+  g_gemv_ws = 4096;
+  CHECK(twl_ternary_linear_noalloc(s8, (float*)P, (uint8_t*)P, s8, (float*)P, 5, 8, 1024, P, TWL_OUT_BF16,
+                                   TWL_PATH_GEMV_MFMA, nullptr) == TWL_OK);
+  CHECK(g_last_ws == g_fake_scratch && g_last_kind == 200 + 10 * twl::kGemvMfma + twl::kOutBf16);
+  // beyond the scratch size: a clear error, nothing launched
+  g_launches = 0;
+  g_gemm_ws = size_t{TWL_NOALLOC_SCRATCH_BYTES} + 1;
+  CHECK(twl_ternary_linear_noalloc(s8, (float*)P, (uint8_t*)P, s8, (float*)P, 64, 8, 1024, P, TWL_OUT_F32,
+                                   TWL_PATH_AUTO, nullptr) == TWL_ESHAPE);
+  CHECK(msg_has("no-allocation scratch") && g_launches == 0);
+  g_gemm_ws = size_t{TWL_NOALLOC_SCRATCH_BYTES};
+  CHECK(twl_ternary_linear_noalloc(s8, (float*)P, (uint8_t*)P, s8, (float*)P, 64, 8, 1024, P, TWL_OUT_F32,
+                                   TWL_PATH_AUTO, nullptr) == TWL_OK);
+  // the same argument checks as twl_ternary_linear_ex
+  CHECK(twl_ternary_linear_noalloc(s8, (float*)P, (uint8_t*)P, s8, (float*)P, 64, 8, 1000, P, TWL_OUT_F32,
+                                   TWL_PATH_AUTO, nullptr) == TWL_ESHAPE);
+  CHECK(twl_ternary_linear_noalloc(s8, nullptr, (uint8_t*)P, s8, (float*)P, 64, 8, 1024, P, TWL_OUT_F32,
+                                   TWL_PATH_AUTO, nullptr) == TWL_EINVAL);
+  CHECK(twl_ternary_linear_noalloc(s8, (float*)P, (uint8_t*)P, s8, (float*)P, 64, 8, 1024, P2, TWL_OUT_F32,
+                                   TWL_PATH_AUTO, nullptr) == TWL_EALIGN);
+  g_gemm_ws = g_gemv_ws = 0;
+  g_device = 0;
+}
+
 }  // namespace
 
 int main() {
   test_validation();
   test_status_mapping();
   test_dispatch_and_workspace();
+  test_noalloc();
   if (g_failures == 0) std::printf("abi_driver: all checks passed\n");
   return g_failures == 0 ? 0 : 1;
 }

@@ -2,7 +2,8 @@
 status mapping, workspace rules) built with AddressSanitizer and
 UndefinedBehaviorSanitizer and driven on the CPU by tests/host/abi_driver.cpp.
 
-The driver replaces the HIP runtime calls api.cpp makes and the kernel
+The driver replaces the HIP runtime calls api.cpp makes (device query,
+properties, error strings, the scratch symbol lookup) and the kernel
 launchers with host stubs, so a failing launch, a failing runtime query and a
 device that is not gfx950 are forced from the host and the mapped status
 (TWL_EHIP, TWL_EDEVICE) and message are checked, together with every shape,
@@ -34,16 +35,21 @@ def driver(tmp_path_factory):
         pytest.skip("ROCm compilers not available")
     d = tmp_path_factory.mktemp("san")
     objs = []
-    for src in (os.path.join(CSRC, "api.cpp"), DRIVER):
+    # api.cpp as the library builds it (its device side holds only the
+    # no-allocation scratch array); the driver as host code only
+    for src, mode in ((os.path.join(CSRC, "api.cpp"), ["--offload-arch=gfx950"]),
+                      (DRIVER, ["--cuda-host-only"])):
         obj = str(d / (os.path.basename(src) + ".o"))
-        cmd = [_hipcc(), "-x", "hip", "--cuda-host-only", "-std=c++17", "-O1", "-g",
-               "-fno-omit-frame-pointer"] + SAN + [
+        cmd = [_hipcc(), "-x", "hip"] + mode + ["-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer"] + SAN + [
             "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c", src, "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)
         assert res.returncode == 0, res.stderr[-3000:]
         objs.append(obj)
     exe = str(d / "abi_driver")
-    link = [CLANG, "-fsanitize=address,undefined"] + objs + ["-o", exe]
+    # the HIP runtime is linked for the code-object registration only: every
+    # runtime call api.cpp makes resolves to the driver's stubs
+    link = [CLANG, "-fsanitize=address,undefined"] + objs + [
+        "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", exe]
     res = subprocess.run(link, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-3000:]
     return exe
