@@ -75,11 +75,53 @@ def n_copies(N: int, K: int) -> int:
     return max(1, -(-CACHE_BUST_BYTES // weight_bytes(N, K)))
 
 
-def graph_time_ms(torch, fn, iters: int, replays: int = 3) -> float:
-    """Mean ms of one fn() call on the GPU: `iters` calls are captured into one
-    HIP graph and the graph is replayed, timed with HIP events on the capture
-    stream.  This removes the host-side launch cost (Python + ctypes, ~10 us
-    per call) that would otherwise hide kernels of a few microseconds."""
+def graph_time_stats(torch, fn, iters: int = 50, replays: int = 10) -> dict:
+    """Per-call GPU time of fn(): `iters` calls are captured into one HIP graph
+    (so host launch cost, ~10 us per call from Python, does not count) and the
+    graph is replayed `replays` times after 2 untimed replays, each replay
+    timed with HIP events on the capture stream.  Returns the median, p10 and
+    p90 over the replays of (replay time / iters), in ms, and the number of
+    timed calls."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(iters):
+            fn()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(replays):
+        with torch.cuda.stream(s):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            g.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / iters)
+    del g
+    per.sort()
+
+    def q(f):
+        return per[min(len(per) - 1, max(0, int(round(f * (len(per) - 1)))))]
+
+    return {"median_ms": q(0.5), "p10_ms": q(0.1), "p90_ms": q(0.9), "calls": iters * replays}
+
+
+def graph_time_ms(torch, fn, iters: int = 50, replays: int = 10) -> float:
+    """Median per-call ms of fn() (graph_time_stats)."""
+    return graph_time_stats(torch, fn, iters, replays)["median_ms"]
+
+
+def _graph_time_best_ms(torch, fn, iters: int, replays: int = 3) -> float:
+    """Best-of-replays variant (kept for the peaks microbenchmarks' read calls)."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -150,16 +192,17 @@ def pages_int8_path(torch, twl, layer, x, sign, packed_q_smax):
     return out
 
 
-def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, kernel_iters=50, bf16=False):
+def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, kernel_iters=50, bf16=False, dot4=False):
     """warmup + timed steps of rotate_quant_act + ternary_linear.
 
     Returns (ms per step from the wall clock around exactly `steps` eager
     steps, the same for the `steps` steps launched as one captured HIP graph,
-    mean ms of one rotate_quant_act launch, mean ms of one ternary_linear call);
-    the per-kernel means come from HIP events around a
-    captured graph of `kernel_iters` back-to-back launches of that kernel alone
-    (weights cycled), see graph_time_ms.  With bf16=True a fourth value is
-    the mean ms of one ternary_linear call that writes y in bf16 instead.
+    the per-call time statistics of rotate_quant_act and of ternary_linear, a
+    dict of further statistics); the per-call statistics come from HIP events
+    around replays of a captured graph of `kernel_iters` back-to-back launches
+    of that call alone (weights cycled), see graph_time_stats.  bf16=True adds
+    "lin16" (y written in bf16), dot4=True adds "dot4" (the decode path forced
+    to the dot4 GEMV).
     """
     M, K = x.shape
     N = sets[0][2].shape[0]
@@ -167,7 +210,7 @@ def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, kernel_iters=50, b
     a_scale = torch.empty((M,), dtype=torch.float32, device="cuda")
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     ws_n = twl.workspace_bytes(M, N, K)
-    ws = torch.zeros(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
 
     def rotq():
         twl.rotate_quant_act(x, sign, out=(x_i8, a_scale))
@@ -206,25 +249,32 @@ def run_layer_steps(torch, twl, x, sign, sets, steps, warmup, kernel_iters=50, b
     ms_graph = (time.perf_counter() - t0) * 1e3 / steps
     del g
 
-    rq = graph_time_ms(torch, rotq, kernel_iters)
+    rq = graph_time_stats(torch, rotq, kernel_iters)
     ctr = [0]
 
     def linear_next():
         linear(ctr[0])
         ctr[0] += 1
 
-    lin = graph_time_ms(torch, linear_next, kernel_iters)
-    if not bf16:
-        return ms_step, ms_graph, rq, lin
-    y16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    lin = graph_time_stats(torch, linear_next, kernel_iters)
+    extra = {}
+    if bf16:
+        y16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
 
-    def linear_bf16_next():
-        packed, q, smax = sets[ctr[0] % len(sets)]
-        twl.ternary_linear_bf16(x_i8, a_scale, packed, q, smax, out=y16, workspace=ws)
-        ctr[0] += 1
+        def linear_bf16_next():
+            packed, q, smax = sets[ctr[0] % len(sets)]
+            twl.ternary_linear_bf16(x_i8, a_scale, packed, q, smax, out=y16, workspace=ws)
+            ctr[0] += 1
 
-    lin16 = graph_time_ms(torch, linear_bf16_next, kernel_iters)
-    return ms_step, ms_graph, rq, lin, lin16
+        extra["lin16"] = graph_time_stats(torch, linear_bf16_next, kernel_iters)
+    if dot4:
+        def linear_dot4_next():
+            packed, q, smax = sets[ctr[0] % len(sets)]
+            twl.ternary_linear(x_i8, a_scale, packed, q, smax, path=twl.PATH_GEMV_DOT4, out=y, workspace=ws)
+            ctr[0] += 1
+
+        extra["dot4"] = graph_time_stats(torch, linear_dot4_next, kernel_iters)
+    return ms_step, ms_graph, rq, lin, extra
 
 
 def traffic_for(kernel_src: str, workload: str):
@@ -300,7 +350,8 @@ def section_layer(torch, twl, name, steps, warmup):
     import workloads as W
     layer = W.make_config(name)
     x, sign, sets = upload_layer(torch, twl, layer, n_copies(layer.N, layer.K))
-    ms, ms_graph, rq, lin, lin16 = run_layer_steps(torch, twl, x, sign, sets, steps, warmup, bf16=True)
+    ms, ms_graph, rqs, lins, ex = run_layer_steps(torch, twl, x, sign, sets, steps, warmup, bf16=True)
+    rq, lin, lin16 = rqs["median_ms"], lins["median_ms"], ex["lin16"]["median_ms"]
     ops = 2.0 * layer.M * layer.N * layer.K
     extra = {}
     if name == "prefill_gate_up":
@@ -331,9 +382,11 @@ def section_layer(torch, twl, name, steps, warmup):
     out = {"M": layer.M, "K": layer.K, "N": layer.N, "ms_per_step": round(ms, 5),
            "step_tops": round(ops / ms / 1e9, 2), "ms_per_step_graph": round(ms_graph, 5),
            "step_tops_graph": round(ops / ms_graph / 1e9, 2), "linear_ms": round(lin, 5),
-           "linear_tops": round(ops / lin / 1e9, 2),
+           "linear_p10_ms": round(lins["p10_ms"], 5), "linear_p90_ms": round(lins["p90_ms"], 5),
+           "linear_calls_timed": lins["calls"], "linear_tops": round(ops / lin / 1e9, 2),
+           "linear_plan": twl.plan_info(layer.M, layer.N, layer.K),
            "linear_bf16_y_ms": round(lin16, 5), "linear_bf16_y_tops": round(ops / lin16 / 1e9, 2),
-           "rotq_ms": round(rq, 5),
+           "rotq_ms": round(rq, 5), "rotq_p10_ms": round(rqs["p10_ms"], 5), "rotq_p90_ms": round(rqs["p90_ms"], 5),
            "rotq_gbs": round((layer.M * layer.K * 3 + layer.M * 4 + layer.K) / rq / 1e6, 1),
            "weight_copies": len(sets), **extra}
     del sets, x
@@ -350,16 +403,28 @@ def section_decode(torch, twl, steps, warmup):
         per_m = {}
         for M in W.DECODE_MS:
             x = x_full[:M].contiguous()
-            ms, ms_graph, rq, lin = run_layer_steps(torch, twl, x, sign, sets, steps, warmup)
+            ms, ms_graph, rqs, lins, ex = run_layer_steps(torch, twl, x, sign, sets, steps, warmup, dot4=True)
+            lin, d4 = lins["median_ms"], ex["dot4"]["median_ms"]
             wb = weight_bytes(layer.N, layer.K)
             tot = wb + M * layer.K + M * 4 + 4 * M * layer.N
+            ops = 2.0 * M * layer.N * layer.K
+            plan = twl.plan_info(M, layer.N, layer.K)
             per_m[str(M)] = {"ms_per_step": round(ms, 5), "ms_per_step_graph": round(ms_graph, 5),
-                             "linear_ms": round(lin, 5),
+                             "kernel": plan["family"],
+                             "linear_ms": round(lin, 5), "linear_p10_ms": round(lins["p10_ms"], 5),
+                             "linear_p90_ms": round(lins["p90_ms"], 5), "linear_calls_timed": lins["calls"],
                              "weight_gbs": round(wb / lin / 1e6, 1),
                              "hbm_frac": round(wb / lin / 1e6 / PEAK_HBM_GBS, 4),
                              "total_gbs": round(tot / lin / 1e6, 1),
-                             "valu_frac": round(2.0 * M * layer.N * layer.K / lin / 1e9 / PEAK_VALU_DOT4_TOPS, 4),
-                             "rotq_ms": round(rq, 5)}
+                             "tops": round(ops / lin / 1e9, 2),
+                             "mfma_frac": round(ops / lin / 1e9 / PEAK_INT8_TOPS, 5),
+                             "dot4_ms": round(d4, 5), "dot4_p10_ms": round(ex["dot4"]["p10_ms"], 5),
+                             "dot4_p90_ms": round(ex["dot4"]["p90_ms"], 5),
+                             "dot4_weight_gbs": round(wb / d4 / 1e6, 1),
+                             "dot4_hbm_frac": round(wb / d4 / 1e6 / PEAK_HBM_GBS, 4),
+                             "dot4_tops": round(ops / d4 / 1e9, 2),
+                             "rotq_ms": round(rqs["median_ms"], 5), "rotq_p10_ms": round(rqs["p10_ms"], 5),
+                             "rotq_p90_ms": round(rqs["p90_ms"], 5)}
         res[name] = {"K": layer.K, "N": layer.N, "by_M": per_m}
         del sets, x_full
         torch.cuda.empty_cache()
@@ -367,7 +432,15 @@ def section_decode(torch, twl, steps, warmup):
 
 
 def section_stack(torch, twl, steps, warmup):
-    """64 decoder layers x {proj 5120->5120, gate_up 5120->34816, down 17408->5120}."""
+    """64 decoder layers x {proj 5120->5120, gate_up 5120->34816, down 17408->5120},
+    one 512-token prefill step and one 24-token decode step, each run two ways:
+      "independent": every linear's input is a pre-drawn activation (rotation
+        + linear per linear, 6 launches per layer);
+      "chained": the down projection takes its input from the gate/up
+        projection of the same layer -- gate/up writes y in bf16 and
+        silu_mul_rotate_quant_act turns it into the down projection's int8
+        input (also 6 launches per layer).
+    Each is timed eagerly (launches from Python) and as one captured HIP graph."""
     import workloads as W
     signs = {k: torch.from_numpy(v).cuda() for k, v in W.stack_signs().items()}
     layers = []
@@ -380,6 +453,7 @@ def section_stack(torch, twl, steps, warmup):
             lin.append((xb, packed, q, smax))
         layers.append(lin)
     torch.cuda.synchronize()
+    inter = W.STACK_LINEARS[2][1]  # 17408: the down projection's input width
     out = {}
     for M in (512, 24):
         bufs = {}
@@ -387,10 +461,11 @@ def section_stack(torch, twl, steps, warmup):
             bufs[which] = (torch.empty((M, K), dtype=torch.int8, device="cuda"),
                            torch.empty((M,), dtype=torch.float32, device="cuda"),
                            torch.empty((M, N), dtype=torch.float32, device="cuda"),
-                           torch.zeros(max(1, twl.workspace_bytes(M, N, K)), dtype=torch.uint8, device="cuda"))
+                           torch.empty(max(1, twl.workspace_bytes(M, N, K)), dtype=torch.uint8, device="cuda"))
+        gu16 = torch.empty((M, 2 * inter), dtype=torch.bfloat16, device="cuda")
         xs = [[lin[w][0][:M].contiguous() for w in range(3)] for lin in layers]
 
-        def step():
+        def step_independent():
             for L, lin in enumerate(layers):
                 for which, (_, packed, q, smax) in enumerate(lin):
                     K = W.STACK_LINEARS[which][1]
@@ -398,37 +473,56 @@ def section_stack(torch, twl, steps, warmup):
                     twl.rotate_quant_act(xs[L][which], signs[K], out=(x_i8, a_scale))
                     twl.ternary_linear(x_i8, a_scale, packed, q, smax, out=y, workspace=ws)
 
-        for _ in range(warmup):
-            step()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            step()
-        torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / steps
-        # the same step captured once as a HIP graph (384 launches) and replayed
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side):
-            step()
-        g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            g.replay()
-        torch.cuda.synchronize()
-        ms_graph = (time.perf_counter() - t0) * 1e3 / steps
-        del g
+        def step_chained():
+            for L, lin in enumerate(layers):
+                for which in (0, 1):
+                    _, packed, q, smax = lin[which]
+                    K = W.STACK_LINEARS[which][1]
+                    x_i8, a_scale, y, ws = bufs[which]
+                    twl.rotate_quant_act(xs[L][which], signs[K], out=(x_i8, a_scale))
+                    if which == 0:
+                        twl.ternary_linear(x_i8, a_scale, packed, q, smax, out=y, workspace=ws)
+                    else:
+                        twl.ternary_linear_bf16(x_i8, a_scale, packed, q, smax, out=gu16, workspace=ws)
+                _, packed, q, smax = lin[2]
+                x_i8, a_scale, y, ws = bufs[2]
+                twl.silu_mul_rotate_quant_act(gu16, signs[inter], out=(x_i8, a_scale))
+                twl.ternary_linear(x_i8, a_scale, packed, q, smax, out=y, workspace=ws)
+
         ops = 2.0 * M * sum(N * K for _, K, N, _, _ in W.STACK_LINEARS) * W.N_LAYERS
         wb = sum(weight_bytes(N, K) for _, K, N, _, _ in W.STACK_LINEARS) * W.N_LAYERS
-        out["prefill_M512" if M == 512 else "decode_M24"] = {
-            "ms_per_step": round(ms, 4), "tops": round(ops / ms / 1e9, 2),
-            "weight_gbs": round(wb / ms / 1e6, 1), "ms_per_step_graph": round(ms_graph, 4),
-            "tops_graph": round(ops / ms_graph / 1e9, 2), "weight_gbs_graph": round(wb / ms_graph / 1e6, 1),
-            "launches": 6 * W.N_LAYERS}
-        del xs, bufs
+        rec = {"launches": 6 * W.N_LAYERS}
+        for mode, step in (("independent", step_independent), ("chained", step_chained)):
+            for _ in range(warmup):
+                step()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / steps
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                step()
+            g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                g.replay()
+            torch.cuda.synchronize()
+            ms_graph = (time.perf_counter() - t0) * 1e3 / steps
+            del g
+            rec[mode] = {"ms_per_step": round(ms, 4), "tops": round(ops / ms / 1e9, 2),
+                         "weight_gbs": round(wb / ms / 1e6, 1), "ms_per_step_graph": round(ms_graph, 4),
+                         "tops_graph": round(ops / ms_graph / 1e9, 2),
+                         "weight_gbs_graph": round(wb / ms_graph / 1e6, 1)}
+        # the previous keys: the independent-input step
+        rec.update({k: rec["independent"][k] for k in rec["independent"]})
+        out["prefill_M512" if M == 512 else "decode_M24"] = rec
+        del xs, bufs, gu16
     del layers
     torch.cuda.empty_cache()
     return out
@@ -501,7 +595,7 @@ def section_peaks(torch):
         check(lib.twl_peak_read(pool.data_ptr() + k * step, wb, 2048, sink.data_ptr(),
                                 torch.cuda.current_stream().cuda_stream), "read call")
 
-    call_ms = graph_time_ms(torch, one, copies)
+    call_ms = _graph_time_best_ms(torch, one, copies)
     del big, pool
     torch.cuda.empty_cache()
     return {"int8_mfma_tops": round(mfma_tops, 1), "int8_mfma_frac_of_spec": round(mfma_tops / PEAK_INT8_TOPS, 4),
@@ -560,14 +654,40 @@ def main(argv=None) -> int:
 
     ops = 2.0 * layer.M * layer.N * layer.K
     achieved = ops / head["linear_ms"] / 1e9
+    plan = head["linear_plan"]
+    r4 = plan["tile_rows"] == 128 and plan["waves"] == 8
+    kname, ksrc = ("gemm_r4_kernel", "gemm_r4.hip") if r4 else ("gemm_kernel", "gemm_i8.hip")
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
                 "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
-                "traffic": traffic_for("gemm_i8.hip", "prefill_gate_up"),
-                "kernel": "gemm_kernel (ternary_linear GEMM path)",
-                "algorithmic_ops_per_launch": ops}
+                "traffic": traffic_for(ksrc, "prefill_gate_up"),
+                "kernel": f"{kname} ({plan['tile_rows']}x{plan['tile_cols']} tiles, "
+                          f"{plan['workgroups']} workgroups, ternary_linear GEMM path)",
+                "algorithmic_ops_per_launch": ops,
+                "launch_ms_median": head["linear_ms"], "launch_ms_p10": head["linear_p10_ms"],
+                "launch_ms_p90": head["linear_p90_ms"], "launches_timed": head["linear_calls_timed"]}
     if peaks:
         roofline["measured_peak"] = peaks["int8_mfma_tops"]
         roofline["frac_of_measured_peak"] = round(achieved / peaks["int8_mfma_tops"], 4)
+    decode_roofline = None
+    if "decode" in detail:
+        # the decode kernel the automatic path takes, against HBM on its
+        # algorithmic weight bytes (the metric's weight GB/s); the forced dot4
+        # GEMV beside it against the measured v_dot4 rate
+        dot4_peak = peaks["valu_dot4_tops"] if peaks else PEAK_VALU_DOT4_TOPS
+        by = {}
+        for lname, rec_l in detail["decode"].items():
+            for m, r in rec_l["by_M"].items():
+                r["dot4_valu_frac"] = round(r["dot4_tops"] / dot4_peak, 4)
+                by[f"{lname} M={m}"] = {"kernel": r["kernel"], "weight_gbs": r["weight_gbs"],
+                                        "frac": r["hbm_frac"], "dot4_weight_gbs": r["dot4_weight_gbs"],
+                                        "dot4_valu_frac": r["dot4_valu_frac"]}
+        g1 = detail["decode"]["decode_gate_up"]["by_M"]["1"]
+        dl = detail["decode"]["decode_gate_up"]
+        decode_roofline = {"bound": "hbm", "kernel": "gemv_rows_kernel (decode path, M <= 24)",
+                           "workload": f"decode_gate_up M=1 K={dl['K']} N={dl['N']}",
+                           "achieved": g1["weight_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": g1["hbm_frac"], "algorithmic_bytes_per_launch": weight_bytes(dl["N"], dl["K"]),
+                           "dot4_peak_tops": dot4_peak, "by_layer_and_M": by}
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
@@ -581,7 +701,7 @@ def main(argv=None) -> int:
                       "step": "rotate_quant_act + ternary_linear",
                       "launch": "eager (graph-launched figure in detail)",
                       "parallelism": "none (1 GPU)"},
-           "roofline": roofline, "cpu_baseline": cpu, "detail": detail}
+           "roofline": roofline, "decode_roofline": decode_roofline, "cpu_baseline": cpu, "detail": detail}
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -84,8 +84,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Wait for this wave's outstanding LDS reads (and scalar loads).
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Wait for this wave's outstanding LDS reads (and scalar loads).  Issued as
+// the builtin, not inline asm: the compiler then knows those reads have
+// landed and does not wait for them again before their first use, which it
+// would do behind the reads issued later (and so wait for those too).
+__device__ __forceinline__ void wait_lgkm0() {
+  // vmcnt 63 and expcnt 7 (no wait), lgkmcnt 0
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
 
 // Workgroup barrier without the memory fence __syncthreads implies: LDS
 // visibility is established by each wave's explicit vmcnt wait before it.
@@ -711,8 +717,10 @@ __global__ __launch_bounds__(64 * 2 * WN * WK, 1) void gemm_kernel(GemmArgs p) {
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[i][t], b, acc[i][j], 0, 0, 0);
         }
       __builtin_amdgcn_s_setprio(0);
+      // this wave's reads of buffer `buf` have landed, on both paths below
+      // (so that at the join the compiler does not wait for them again)
+      wait_lgkm0();
       if (st + 1 < st_end) {
-        wait_lgkm0();  // this wave's reads of buffer `buf` have landed
         wait_vmcnt<(S - 2) * T::LOADS_PER_STAGE>();  // own loads of stage st+1 done
         bare_barrier();  // everyone's stage st+1 is in LDS; everyone is past buffer `buf`
         read_a(nbuf, 0, a0);

@@ -21,7 +21,8 @@ from ternary_weight_linear_block_amd import build as B
 
 # source file -> (kernel whose instantiations set M0 from inline asm, the
 # least number of instantiations expected)
-M0_KERNELS = {"gemm_i8.hip": ("gemm_kernel", 10), "gemv.hip": ("gemv_rows_kernel", 15)}
+M0_KERNELS = {"gemm_i8.hip": ("gemm_kernel", 10),
+              "gemv.hip": ("gemv_rows_kernel", 15)}
 
 
 def _compile_asm(tmp_path_factory, src):
