@@ -345,6 +345,27 @@ def copy_calibration(torch) -> int:
     return 0
 
 
+def kernel_only(torch, twl, name, launches, decode_m) -> int:
+    """Launches ternary_linear alone on one workload `launches` times (weights
+    cycled through the cache-busting copies, inputs resident), for rocprofv3
+    runs; prints the plan and the launch count."""
+    import workloads as W
+    layer = W.make_config(name)
+    x, sign, sets = upload_layer(torch, twl, layer, n_copies(layer.N, layer.K))
+    M = decode_m if name.startswith("decode") else layer.M
+    x = x[:M].contiguous()
+    x_i8, a_scale = twl.rotate_quant_act(x, sign)
+    y = torch.empty((M, layer.N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, twl.workspace_bytes(M, layer.N, layer.K)), dtype=torch.uint8, device="cuda")
+    for i in range(launches):
+        packed, q, smax = sets[i % len(sets)]
+        twl.ternary_linear(x_i8, a_scale, packed, q, smax, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel_only": name, "M": M, "K": layer.K, "N": layer.N, "launches": launches,
+                      "plan": twl.plan_info(M, layer.N, layer.K)}), flush=True)
+    return 0
+
+
 def section_layer(torch, twl, name, steps, warmup):
     import numpy as np
     import workloads as W
@@ -534,7 +555,9 @@ def section_peaks(torch):
     int8 MFMA rate (the GEMM's instruction with no memory traffic), the HBM
     read rate (nontemporal stream of 1 GiB), the time of one streaming read of
     the decode weight size (22.3 MB, graph-captured back to back like the
-    decode calls), and the VALU v_dot4 int8 rate."""
+    decode calls), the VALU v_dot4 int8 rate, and the rate of the prefill
+    GEMM's MFMA + 2-bit unpack instruction mix without memory traffic (each
+    unpacked operand feeding 2 or 4 MFMAs)."""
     import ctypes
     from ternary_weight_linear_block_amd.build import PEAKS_LIB_PATH
     if not os.path.exists(PEAKS_LIB_PATH):
@@ -545,7 +568,8 @@ def section_peaks(torch):
     lib.twl_peak_mfma_i8.argtypes = [I, I, P, P]
     lib.twl_peak_read.argtypes = [P, S, I, P, P]
     lib.twl_peak_dot4.argtypes = [I, I, P, P]
-    for f in (lib.twl_peak_mfma_i8, lib.twl_peak_read, lib.twl_peak_dot4):
+    lib.twl_peak_mix_i8.argtypes = [I, I, I, P, P]
+    for f in (lib.twl_peak_mfma_i8, lib.twl_peak_read, lib.twl_peak_dot4, lib.twl_peak_mix_i8):
         f.restype = I
     sink = torch.zeros(16, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -573,6 +597,12 @@ def section_peaks(torch):
     wgs, iters = 1024, 2000
     ms = timed(lambda: check(lib.twl_peak_mfma_i8(wgs, iters, sink.data_ptr(), h), "mfma peak"))
     mfma_tops = 2.0 * 32 * 32 * 32 * 10 * iters * wgs * 4 / (ms * 1e-3) / 1e12
+    # the GEMM's MFMA + unpack mix, one workgroup per CU: 3 waves per SIMD
+    # with 2 x 3 fragments (reuse 2), 2 waves per SIMD with 4 x 2 (reuse 4)
+    mix = {}
+    for reuse, frags, wps in ((2, 6, 3), (4, 8, 2)):
+        ms = timed(lambda: check(lib.twl_peak_mix_i8(reuse, 256, iters, sink.data_ptr(), h), "mix peak"))
+        mix[reuse] = 2.0 * 32 * 32 * 32 * frags * iters * 256 * 4 * wps / (ms * 1e-3) / 1e12
     ms = timed(lambda: check(lib.twl_peak_dot4(wgs, iters, sink.data_ptr(), h), "dot4 peak"))
     dot4_tops = 8.0 * 8 * iters * wgs * 256 / (ms * 1e-3) / 1e12
     big = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
@@ -601,7 +631,8 @@ def section_peaks(torch):
     return {"int8_mfma_tops": round(mfma_tops, 1), "int8_mfma_frac_of_spec": round(mfma_tops / PEAK_INT8_TOPS, 4),
             "hbm_read_gbs": round(read_gbs, 1), "hbm_read_frac_of_spec": round(read_gbs / PEAK_HBM_GBS, 4),
             "decode_size_read_us": round(call_ms * 1e3, 2), "decode_size_read_bytes": wb,
-            "valu_dot4_tops": round(dot4_tops, 1)}
+            "valu_dot4_tops": round(dot4_tops, 1),
+            "mfma_unpack_mix_reuse2_tops": round(mix[2], 1), "mfma_unpack_mix_reuse4_tops": round(mix[4], 1)}
 
 
 def main(argv=None) -> int:
@@ -612,6 +643,12 @@ def main(argv=None) -> int:
     ap.add_argument("--sections", default=",".join(SECTIONS),
                     help="comma list of: " + ", ".join(SECTIONS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--kernel-only", default=None,
+                    help="only launch ternary_linear on one workload (prefill_gate_up, prefill_down, "
+                         "decode_gate_up, decode_down) --launches times, weights cycled, and exit: "
+                         "the run that rocprofv3 counter passes profile")
+    ap.add_argument("--launches", type=int, default=20)
+    ap.add_argument("--decode-m", type=int, default=1, help="tokens for --kernel-only decode_*")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a copy-like kernel of known traffic (y = -x over 1 GiB of "
                          "float32, 3 launches) to scale HBM byte counters, then exit")
@@ -631,6 +668,8 @@ def main(argv=None) -> int:
         return 2
     if args.copy_calibration:
         return copy_calibration(torch)
+    if args.kernel_only:
+        return kernel_only(torch, twl, args.kernel_only, args.launches, args.decode_m)
     sections = [s for s in args.sections.split(",") if s]
     detail = {"device": torch.cuda.get_device_name(0)}
 

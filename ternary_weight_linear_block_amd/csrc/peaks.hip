@@ -10,6 +10,9 @@
 //                      workgroup streaming one contiguous chunk: the HBM read
 //                      rate, and at the decode weight size (22.3 MB) the time
 //                      floor of one streaming call.
+//   twl_peak_mix_i8    the prefill GEMM's MFMA + 2-bit unpack instruction mix
+//                      without memory traffic, each unpacked operand feeding
+//                      2 or 4 MFMAs: the rate that mix sustains.
 //   twl_peak_dot4      chains of v_dot4_i32_iu8 on eight independent
 //                      accumulators per lane: the VALU int8 dot-product rate.
 //
@@ -86,9 +89,82 @@ __global__ __launch_bounds__(256) void peak_dot4_kernel(int iters, int* sink) {
   if (s == 0x7FFFFFF1) sink[0] = s;
 }
 
+// The GEMM's inner instruction mix without memory traffic: per column
+// fragment one packed word unpacked to 16 int8 weights by the 9-operation
+// permute sequence (1 shift, 4 ANDs, 4 v_perm_b32 against {-q, +q, 0}
+// tables), feeding RM MFMAs (one per row fragment), RN column fragments per
+// wave, WPS waves per SIMD.  The word rotates every iteration so the unpack
+// is not hoisted.  Gives the int8 rate this part sustains when each unpacked
+// operand is reused RM times, with the clock the mix runs at.
+__device__ __forceinline__ v4i mix_unpack(uint32_t w, uint32_t ta, uint32_t tb0, uint32_t tb1) {
+  const uint32_t w4 = w >> 4;
+  v4i b;
+  b.x = static_cast<int>(__builtin_amdgcn_perm(0u, ta, w & 0x03030303u));
+  b.y = static_cast<int>(__builtin_amdgcn_perm(tb0, tb1, w & 0x0C0C0C0Cu));
+  b.z = static_cast<int>(__builtin_amdgcn_perm(0u, ta, w4 & 0x03030303u));
+  b.w = static_cast<int>(__builtin_amdgcn_perm(tb0, tb1, w4 & 0x0C0C0C0Cu));
+  return b;
+}
+
+template <int RM, int RN, int WPS>
+__global__ __launch_bounds__(256 * WPS, 1) void peak_mix_kernel(int iters, int* sink) {
+  const int lane = threadIdx.x & 63;
+  v16i acc[RM][RN];
+#pragma unroll
+  for (int i = 0; i < RM; ++i)
+#pragma unroll
+    for (int j = 0; j < RN; ++j) acc[i][j] = v16i{0};
+  v4i a[RM];
+#pragma unroll
+  for (int i = 0; i < RM; ++i) a[i] = v4i{lane + i, lane * 3 + i, lane ^ (5 + i), lane + 11 * i};
+  uint32_t w[RN], ta[RN], tb0[RN], tb1[RN];
+#pragma unroll
+  for (int j = 0; j < RN; ++j) {
+    w[j] = 0x9E3779B9u * static_cast<uint32_t>(lane + 7 * j + 1);
+    const uint32_t q = static_cast<uint32_t>(17 + 9 * j), neg = 0u - q;
+    ta[j] = __builtin_amdgcn_perm(q, neg, 0x0C0C0400u);
+    tb0[j] = q;
+    tb1[j] = __builtin_amdgcn_perm(0u, neg, 0x0C0C0C00u);
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < RN; ++j) {
+      const v4i b = mix_unpack(w[j], ta[j], tb0[j], tb1[j]);
+      w[j] = __builtin_amdgcn_alignbit(w[j], w[j], 3);
+#pragma unroll
+      for (int i = 0; i < RM; ++i) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b, acc[i][j], 0, 0, 0);
+    }
+  }
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < RM; ++i)
+#pragma unroll
+    for (int j = 0; j < RN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s ^= acc[i][j][r];
+  if (s == 0x7FFFFFF1) sink[0] = s;
+}
+
 }  // namespace
 
 extern "C" {
+
+// The GEMM's MFMA + unpack mix (no memory traffic).  reuse 2: 2 row
+// fragments x 3 column fragments per wave, 3 waves per SIMD (the 12-wave
+// prefill tile); reuse 4: 4 x 2, 2 waves per SIMD.  One workgroup per CU.
+// Operations of one call: 2 * 32^3 * (row x column fragments) * iters per
+// wave, 4 * WPS waves per workgroup.
+int twl_peak_mix_i8(int reuse, int workgroups, int iters, int* sink, hipStream_t stream) {
+  if (workgroups <= 0 || iters <= 0 || sink == nullptr || (reuse != 2 && reuse != 4))
+    return static_cast<int>(hipErrorInvalidValue);
+  if (reuse == 2)
+    hipLaunchKernelGGL((peak_mix_kernel<2, 3, 3>), dim3(static_cast<unsigned>(workgroups)), dim3(768), 0,
+                       stream, iters, sink);
+  else
+    hipLaunchKernelGGL((peak_mix_kernel<4, 2, 2>), dim3(static_cast<unsigned>(workgroups)), dim3(512), 0,
+                       stream, iters, sink);
+  return static_cast<int>(hipGetLastError());
+}
 
 // Operations of one call: 2 * 32 * 32 * 32 * 10 * iters per wave, 4 waves per
 // workgroup (one per SIMD).

@@ -113,5 +113,5 @@ def test_peaks_library_exports_its_microbenchmarks():
     if not os.path.exists(PEAKS_LIB_PATH):
         pytest.skip("libtwl_peaks.so not built")
     lib = ctypes.CDLL(PEAKS_LIB_PATH)
-    for name in ("twl_peak_mfma_i8", "twl_peak_read", "twl_peak_dot4"):
+    for name in ("twl_peak_mfma_i8", "twl_peak_read", "twl_peak_dot4", "twl_peak_mix_i8"):
         assert hasattr(lib, name), name
