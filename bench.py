@@ -694,12 +694,10 @@ def main(argv=None) -> int:
     ops = 2.0 * layer.M * layer.N * layer.K
     achieved = ops / head["linear_ms"] / 1e9
     plan = head["linear_plan"]
-    r4 = plan["tile_rows"] == 128 and plan["waves"] == 8
-    kname, ksrc = ("gemm_r4_kernel", "gemm_r4.hip") if r4 else ("gemm_kernel", "gemm_i8.hip")
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
                 "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
-                "traffic": traffic_for(ksrc, "prefill_gate_up"),
-                "kernel": f"{kname} ({plan['tile_rows']}x{plan['tile_cols']} tiles, "
+                "traffic": traffic_for("gemm_i8.hip", "prefill_gate_up"),
+                "kernel": f"gemm_kernel ({plan['tile_rows']}x{plan['tile_cols']} tiles, "
                           f"{plan['workgroups']} workgroups, ternary_linear GEMM path)",
                 "algorithmic_ops_per_launch": ops,
                 "launch_ms_median": head["linear_ms"], "launch_ms_p10": head["linear_p10_ms"],
@@ -726,6 +724,7 @@ def main(argv=None) -> int:
                            "workload": f"decode_gate_up M=1 K={dl['K']} N={dl['N']}",
                            "achieved": g1["weight_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": g1["hbm_frac"], "algorithmic_bytes_per_launch": weight_bytes(dl["N"], dl["K"]),
+                           "traffic": traffic_for("gemv.hip", "decode_gate_up_m1"),
                            "dot4_peak_tops": dot4_peak, "by_layer_and_M": by}
     cpu = None
     if not args.no_cpu:
