@@ -415,6 +415,23 @@ def section_layer(torch, twl, name, steps, warmup):
     return layer, out
 
 
+def fused_stats(torch, twl, x, sign, sets, iters: int = 50) -> dict:
+    """Per-call time of rotate_quant_linear (the rotation and the decode kernel
+    fused into one launch) from bf16 x, weights cycled, as graph_time_stats."""
+    M, K = x.shape
+    N = sets[0][2].shape[0]
+    x_i8 = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    a_scale = torch.empty((M,), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ctr = [0]
+
+    def call():
+        packed, q, smax = sets[ctr[0] % len(sets)]
+        ctr[0] += 1
+        twl.rotate_quant_linear(x, sign, packed, q, smax, out=y, x_i8=x_i8, a_scale=a_scale)
+    return graph_time_stats(torch, call, iters)
+
+
 def section_decode(torch, twl, steps, warmup):
     import workloads as W
     res = {}
@@ -446,6 +463,13 @@ def section_decode(torch, twl, steps, warmup):
                              "dot4_tops": round(ops / d4 / 1e9, 2),
                              "rotq_ms": round(rqs["median_ms"], 5), "rotq_p10_ms": round(rqs["p10_ms"], 5),
                              "rotq_p90_ms": round(rqs["p90_ms"], 5)}
+            if twl.rotate_quant_linear_fused(M, layer.N, layer.K):
+                # the same step as one fused launch (rotate_quant_linear)
+                fz = fused_stats(torch, twl, x, sign, sets)
+                per_m[str(M)].update({"fused_step_ms": round(fz["median_ms"], 5),
+                                      "fused_step_p10_ms": round(fz["p10_ms"], 5),
+                                      "fused_step_p90_ms": round(fz["p90_ms"], 5),
+                                      "fused_weight_gbs": round(wb / fz["median_ms"] / 1e6, 1)})
         res[name] = {"K": layer.K, "N": layer.N, "by_M": per_m}
         del sets, x_full
         torch.cuda.empty_cache()
@@ -718,6 +742,8 @@ def main(argv=None) -> int:
                 by[f"{lname} M={m}"] = {"kernel": r["kernel"], "weight_gbs": r["weight_gbs"],
                                         "frac": r["hbm_frac"], "dot4_weight_gbs": r["dot4_weight_gbs"],
                                         "dot4_valu_frac": r["dot4_valu_frac"]}
+                if "fused_step_ms" in r:
+                    by[f"{lname} M={m}"]["fused_step_ms"] = r["fused_step_ms"]
         g1 = detail["decode"]["decode_gate_up"]["by_M"]["1"]
         dl = detail["decode"]["decode_gate_up"]
         decode_roofline = {"bound": "hbm", "kernel": "gemv_rows_kernel (decode path, M <= 24)",

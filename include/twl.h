@@ -260,6 +260,43 @@ twl_status twl_ternary_linear_noalloc(const int8_t* x_i8, const float* a_scale,
  */
 twl_status twl_plan_info(int64_t M, int64_t N, int64_t K, int path, int64_t* info);
 
+/*
+ * rotate_quant_linear -- a whole ternary linear layer from its bf16 input:
+ * rotate_quant_act ([P1] Prerequisites, sections 1 and 4; with silu = 1
+ * silu_mul_rotate_quant_act, x then being the gate/up output [M, 2K]) followed
+ * by ternary_linear_ex with TWL_PATH_AUTO ([P1] section 4 for prefill, section
+ * 5 for decode).  x_i8, a_scale and out are all written and are bit-identical
+ * to what the two calls produce.
+ *   x         in : bf16 bit patterns [M, K] (silu = 1: [M, 2K])
+ *   sign      in : int8 +-1 [K]
+ *   packed, q, smax in: as ternary_linear
+ *   x_i8      out: int8 [M, K];  a_scale out: fp32 [M]  (device, caller-owned)
+ *   out       out: [M, N] of the out_kind (twl_out)
+ *   workspace     : as ternary_linear_ex for this M, N, K (twl_workspace_bytes)
+ * For small decode batches (at most 4 tokens, K <= 17408, at most 3 1024-blocks
+ * of rotation per wave of a decode workgroup, on shapes where the row-balanced
+ * decode kernel applies) one fused kernel does both steps: every decode
+ * workgroup rotates and quantises the tokens itself while its first weight
+ * loads are in flight, which removes the rotation's own launch from the
+ * decode step.  Other shapes run the two kernels back to back on `stream`.
+ * twl_rotate_quant_linear_fused tells which applies.  Errors: those of both
+ * steps, checked before anything is enqueued; TWL_EINVAL for silu not 0 or 1.
+ * M = 0 is a no-op; N = 0 writes only x_i8 and a_scale.
+ */
+twl_status twl_rotate_quant_linear(const uint16_t* x, const int8_t* sign, const uint8_t* packed,
+                                   const int8_t* q, const float* smax, int64_t M, int64_t N,
+                                   int64_t K, int silu, int8_t* x_i8, float* a_scale, void* out,
+                                   int out_kind, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/*
+ * rotate_quant_linear_fused -- 1 when twl_rotate_quant_linear runs this shape
+ * as one fused kernel on the current device, 0 when it runs the two steps, or
+ * a negative twl_status (-TWL_ESHAPE, -TWL_EDEVICE, ...) for a shape or device
+ * it rejects.
+ */
+int twl_rotate_quant_linear_fused(int64_t M, int64_t N, int64_t K);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* twl_last_error(void);
 

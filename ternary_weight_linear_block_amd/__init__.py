@@ -22,7 +22,7 @@ from ._lib import (GEMV_MAX_M, GROUP, HBLOCK, MAX_K, PATH_AUTO, PATH_GEMM, PATH_
 __all__ = [
     "rotate_quant_act", "silu_mul_rotate_quant_act", "pack_ternary", "rotate_act_bf16",
     "reference_linear_bf16", "ternary_linear", "ternary_linear_acc", "ternary_linear_bf16",
-    "ternary_linear_noalloc",
+    "ternary_linear_noalloc", "rotate_quant_linear", "rotate_quant_linear_fused",
     "workspace_bytes", "packed_bytes", "plan_info", "TwlError", "PATH_AUTO", "PATH_GEMM", "PATH_GEMV", "PATH_GEMV_DOT4",
     "PATH_GEMV_MFMA", "GEMV_MAX_M",
     "HBLOCK", "GROUP", "MAX_K", "library",
@@ -253,6 +253,64 @@ def ternary_linear_noalloc(x_i8, a_scale, packed, q, smax, out, path: int = PATH
         M, N, K, _dev_ptr(out, "out", (out.dtype,)), out_kind, path, _stream_handle(stream))
     _lib.check(st, "twl_ternary_linear_noalloc")
     return out
+
+
+def rotate_quant_linear_fused(M: int, N: int, K: int) -> bool:
+    """Whether rotate_quant_linear runs this shape as one fused kernel on the
+    current device (twl_rotate_quant_linear_fused)."""
+    r = int(_lib.load().twl_rotate_quant_linear_fused(M, N, K))
+    if r < 0:
+        _lib.check(-r, "twl_rotate_quant_linear_fused")
+    return r == 1
+
+
+def rotate_quant_linear(x, sign, packed, q, smax, silu: bool = False, out=None, out_dtype=None,
+                        x_i8=None, a_scale=None, workspace=None, stream=None):
+    """A whole layer from its bf16 input (twl_rotate_quant_linear):
+    rotate_quant_act (silu: of bf16(SiLU(gate) * up), x being [gate | up]
+    [M, 2K]) then ternary_linear with the automatic path, as one fused decode
+    kernel for small batches.  Returns (out, x_i8, a_scale); out is y in
+    out_dtype (float32 unless given: bfloat16, or int32 for the raw
+    accumulators) or the given `out`, whose dtype then sets the kind."""
+    torch = _torch()
+    lib = _lib.load()
+    M, KX = x.shape
+    if silu and KX % 2:
+        raise ValueError(f"x has {KX} columns, expected 2K with silu")
+    K = KX // 2 if silu else KX
+    N = q.shape[0]
+    if q.dim() != 2 or q.shape[1] * GROUP != K:
+        raise ValueError(f"q has shape {tuple(q.shape)}, expected [N, K/128] with K = {K}")
+    if N > 0 and packed.numel() != packed_bytes(N, K):
+        raise ValueError(f"packed has {packed.numel()} bytes, expected {packed_bytes(N, K)}")
+    kinds = {torch.float32: _lib.OUT_F32, torch.int32: _lib.OUT_ACC_I32, torch.bfloat16: _lib.OUT_BF16}
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32 if out_dtype is None else out_dtype, device=x.device)
+    if out.dtype not in kinds:
+        raise TypeError(f"out has dtype {out.dtype}, expected float32, bfloat16 or int32")
+    out_kind = kinds[out.dtype]
+    if x_i8 is None:
+        x_i8 = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if a_scale is None:
+        a_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    stream_handle = _stream_handle(stream)
+    ws_ptr, ws_len = None, 0
+    if M > 0 and N > 0 and not rotate_quant_linear_fused(M, N, K):
+        need = workspace_bytes(M, N, K)
+        if need:
+            if workspace is None:
+                workspace = _default_workspace(need, x.device, stream_handle)
+            ws_ptr, ws_len = _dev_ptr(workspace, "workspace", (torch.uint8,)), workspace.numel()
+    out_acc = out_kind == _lib.OUT_ACC_I32
+    st = lib.twl_rotate_quant_linear(
+        _dev_ptr(x, "x", (torch.bfloat16, torch.int16)), _dev_ptr(sign, "sign", (torch.int8,)),
+        _dev_ptr(packed, "packed", (torch.uint8,)), _dev_ptr(q, "q", (torch.int8,)),
+        None if out_acc else _dev_ptr(smax, "smax", (torch.float32,)),
+        M, N, K, 1 if silu else 0, _dev_ptr(x_i8, "x_i8", (torch.int8,)),
+        _dev_ptr(a_scale, "a_scale", (torch.float32,)), _dev_ptr(out, "out", (out.dtype,)),
+        out_kind, ws_ptr, ws_len, stream_handle)
+    _lib.check(st, "twl_rotate_quant_linear")
+    return out, x_i8, a_scale
 
 
 def ternary_linear(x_i8, a_scale, packed, q, smax, path: int = PATH_AUTO, out=None,

@@ -39,6 +39,9 @@ SIGNATURES = [
     ("twl_ternary_linear_noalloc", _INT,
      [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _INT, _INT, _P]),
     ("twl_plan_info", _INT, [_I64, _I64, _I64, _INT, _P]),
+    ("twl_rotate_quant_linear", _INT,
+     [_P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _P, _P, _INT, _P, _SIZE, _P]),
+    ("twl_rotate_quant_linear_fused", _INT, [_I64, _I64, _I64]),
     ("twl_last_error", ctypes.c_char_p, []),
     ("twl_abi_version", _INT, []),
 ]

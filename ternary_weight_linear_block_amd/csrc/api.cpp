@@ -122,6 +122,29 @@ twl_status current_scratch(void** out) {
   return TWL_OK;
 }
 
+twl::GemvKind gemv_kind(int path) {
+  return path == TWL_PATH_GEMV_DOT4   ? twl::kGemvDot4
+         : path == TWL_PATH_GEMV_MFMA ? twl::kGemvMfma
+                                      : twl::kGemvAuto;
+}
+
+// Bytes of K-split partial sums the linear layer needs for this shape and
+// path (0 when it does not split K).
+size_t workspace_need(int64_t M, int64_t N, int64_t K, int path, const twl::DeviceInfo& dev) {
+  const bool use_gemv = path >= TWL_PATH_GEMV || (path == TWL_PATH_AUTO && M <= TWL_GEMV_MAX_M);
+  return use_gemv ? twl::gemv_workspace_bytes(M, N, K, gemv_kind(path), dev)
+                  : twl::gemm_workspace_bytes(M, N, K, dev);
+}
+
+twl_status check_workspace(size_t need, const void* workspace, size_t workspace_bytes) {
+  if (need == 0) return TWL_OK;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(TWL_EINVAL, "workspace of %zu bytes required (got %zu)", need,
+                workspace == nullptr ? size_t{0} : workspace_bytes);
+  if (!aligned16(workspace)) return fail(TWL_EALIGN, "workspace is not 16-byte aligned");
+  return TWL_OK;
+}
+
 // The linear layer with the K-split partial sums either in the caller's
 // workspace or (use_scratch) in the library's per-device scratch.
 twl_status linear_impl(const int8_t* x_i8, const float* a_scale, const uint8_t* packed,
@@ -151,11 +174,8 @@ twl_status linear_impl(const int8_t* x_i8, const float* a_scale, const uint8_t* 
   twl::DeviceInfo dev;
   TWL_TRY(current_device(&dev));
   const bool use_gemv = decode_path || (path == TWL_PATH_AUTO && M <= TWL_GEMV_MAX_M);
-  const twl::GemvKind kind = path == TWL_PATH_GEMV_DOT4   ? twl::kGemvDot4
-                             : path == TWL_PATH_GEMV_MFMA ? twl::kGemvMfma
-                                                          : twl::kGemvAuto;
-  const size_t part = use_gemv ? twl::gemv_workspace_bytes(M, N, K, kind, dev)
-                               : twl::gemm_workspace_bytes(M, N, K, dev);
+  const twl::GemvKind kind = gemv_kind(path);
+  const size_t part = workspace_need(M, N, K, path, dev);
   if (use_scratch) {
     if (part > TWL_NOALLOC_SCRATCH_BYTES)
       return fail(TWL_ESHAPE,
@@ -169,11 +189,8 @@ twl_status linear_impl(const int8_t* x_i8, const float* a_scale, const uint8_t* 
       TWL_TRY(current_scratch(&workspace));
       workspace_bytes = TWL_NOALLOC_SCRATCH_BYTES;
     }
-  } else if (part > 0) {
-    if (workspace == nullptr || workspace_bytes < part)
-      return fail(TWL_EINVAL, "workspace of %zu bytes required (got %zu)", part,
-                  workspace == nullptr ? size_t{0} : workspace_bytes);
-    if (!aligned16(workspace)) return fail(TWL_EALIGN, "workspace is not 16-byte aligned");
+  } else {
+    TWL_TRY(check_workspace(part, workspace, workspace_bytes));
   }
   if (use_gemv)
     return launched(twl::launch_gemv(x_i8, a_scale, packed, q, smax, M, N, K, out,
@@ -308,6 +325,56 @@ twl_status twl_ternary_linear_noalloc(const int8_t* x_i8, const float* a_scale,
                      true, stream);
 }
 
+twl_status twl_rotate_quant_linear(const uint16_t* x, const int8_t* sign, const uint8_t* packed,
+                                   const int8_t* q, const float* smax, int64_t M, int64_t N,
+                                   int64_t K, int silu, int8_t* x_i8, float* a_scale, void* out,
+                                   int out_kind, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  TWL_TRY(check_rows("M", M));
+  TWL_TRY(check_rows("N", N));
+  TWL_TRY(check_k(K));
+  if (silu != 0 && silu != 1) return fail(TWL_EINVAL, "silu must be 0 or 1 (got %d)", silu);
+  if (out_kind < TWL_OUT_F32 || out_kind > TWL_OUT_BF16)
+    return fail(TWL_EINVAL, "unknown output kind %d", out_kind);
+  if (M == 0) return ok();
+  TWL_REQUIRE_PTR(x);
+  TWL_REQUIRE_PTR(sign);
+  TWL_REQUIRE_PTR(x_i8);
+  TWL_REQUIRE_PTR(a_scale);
+  if (N > 0) {
+    TWL_REQUIRE_PTR(packed);
+    TWL_REQUIRE_PTR(q);
+    TWL_REQUIRE_PTR(out);
+    if (out_kind != TWL_OUT_ACC_I32) TWL_REQUIRE_PTR(smax);
+  }
+  twl::DeviceInfo dev;
+  TWL_TRY(current_device(&dev));
+  if (N > 0 && twl::gemv_rot_applies(M, N, K, dev))
+    return launched(twl::launch_gemv_rot(x, sign, silu != 0, packed, q, smax, M, N, K, out,
+                                         static_cast<twl::OutKind>(out_kind), x_i8, a_scale, dev,
+                                         stream),
+                    "rotate_quant_linear (fused decode)");
+  // two steps; the linear step's workspace is checked before anything is enqueued
+  if (N > 0) TWL_TRY(check_workspace(workspace_need(M, N, K, TWL_PATH_AUTO, dev), workspace, workspace_bytes));
+  TWL_TRY(launched(silu ? twl::launch_silu_mul_rotate_quant(x, sign, M, K, x_i8, a_scale, stream)
+                        : twl::launch_rotate_quant(x, sign, M, K, x_i8, a_scale, stream),
+                   "rotate_quant_linear (rotation)"));
+  if (N == 0) return ok();
+  return linear_impl(x_i8, a_scale, packed, q, smax, M, N, K, out, out_kind, TWL_PATH_AUTO, workspace,
+                     workspace_bytes, false, stream);
+}
+
+int twl_rotate_quant_linear_fused(int64_t M, int64_t N, int64_t K) {
+  twl_status st = check_rows("M", M);
+  if (st == TWL_OK) st = check_rows("N", N);
+  if (st == TWL_OK) st = check_k(K);
+  twl::DeviceInfo dev;
+  if (st == TWL_OK) st = current_device(&dev);
+  if (st != TWL_OK) return -static_cast<int>(st);
+  ok();
+  return M > 0 && N > 0 && twl::gemv_rot_applies(M, N, K, dev) ? 1 : 0;
+}
+
 twl_status twl_plan_info(int64_t M, int64_t N, int64_t K, int path, int64_t* info) {
   TWL_TRY(check_rows("M", M));
   TWL_TRY(check_rows("N", N));
@@ -325,10 +392,7 @@ twl_status twl_plan_info(int64_t M, int64_t N, int64_t K, int path, int64_t* inf
   TWL_TRY(current_device(&dev));
   const bool use_gemv = decode_path || (path == TWL_PATH_AUTO && M <= TWL_GEMV_MAX_M);
   if (use_gemv) {
-    const twl::GemvKind kind = path == TWL_PATH_GEMV_DOT4   ? twl::kGemvDot4
-                               : path == TWL_PATH_GEMV_MFMA ? twl::kGemvMfma
-                                                            : twl::kGemvAuto;
-    twl::gemv_plan_info(M, N, K, kind, dev, info);
+    twl::gemv_plan_info(M, N, K, gemv_kind(path), dev, info);
   } else {
     twl::gemm_plan_info(M, N, K, dev, info);
   }

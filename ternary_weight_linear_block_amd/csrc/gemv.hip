@@ -38,7 +38,7 @@
 //   workgroup) and is used at every M whenever each CU gets at least 16 rows;
 //   gemv_mfma_kernel keeps the 64-row-block split with K slices (4 <= M <= 24)
 //   for layers with fewer rows per CU.
-#include "twl_internal.h"
+#include "rotate_block.h"
 
 #include <algorithm>
 #include <cstdio>
@@ -95,6 +95,14 @@ struct GemvArgs {
   int n_rb;           // 64-row blocks
   int slices;         // workgroups per row block (K split across workgroups)
   int out_kind;       // OutKind
+  // fused rotation (gemv_rows_kernel with ROT): the kernel quantises its own
+  // activations from bf16 x [M, K] (with silu, [gate | up] [M, 2K]) and writes
+  // x_i8 [M, K] and a_scale [M] from workgroup 0
+  const uint16_t* xb;
+  const int8_t* sign;
+  int8_t* x_i8_out;
+  float* a_scale_out;
+  int silu;
 };
 
 // v_permlane32_swap_b32 exchanges lanes 32..63 of its first operand with lanes
@@ -414,18 +422,35 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(GemvArgs a, int M) {
 constexpr int kXRows = 24;              // the decode paths take M <= 24
 constexpr int kXSlot = kXRows * 128;    // bytes per group slot
 constexpr int kRowsMaxWaves = 8;
+// Fused rotation (ROT): at most kRotMaxM tokens of at most kRotMaxK, each wave
+// rotating at most kRotBlocksPerWave 1024-blocks; all of x_i8 then stays in
+// LDS, rows padded by 16 bytes (so that the tokens' 16-byte reads fall on
+// different banks).
+constexpr int kRotMaxM = 4;
+constexpr int kRotMaxK = 17408;
+constexpr int kRotBlocksPerWave = 3;
+constexpr int kRotXBytes = kRotMaxM * (kRotMaxK + 16);
 
 template <int NS>
 struct RowGroup {
   uint4 w[NS];   // 16 packed bytes of row 32 s + j, half h
 };
 
-template <int NS, int GMAX, int P, int MAXT>
+// ROT: the workgroup first rotates and quantises the M <= kRotMaxM tokens
+// itself (every workgroup, redundantly: at most kRotBlocksPerWave blocks per
+// wave), while its first P groups of weights are already in flight; x_i8 then
+// stays in LDS for the whole K and no activation is loaded per group.  The
+// rotation and the quantiser are those of rotate_quant_act (rotate_block.h),
+// so x_i8, a_scale and y equal the two-step result bit for bit.
+template <int NS, int GMAX, int P, int MAXT, bool ROT = false>
 __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
   static_assert(P >= 1 && P <= GMAX, "prefetch depth");
   static_assert(MAXT <= 64 * kRowsMaxWaves, "x slots are sized for 8 waves");
   __shared__ int red[32 * NS * kRedStride];
-  __shared__ __attribute__((aligned(1024))) int8_t xs[kRowsMaxWaves * P * kXSlot];
+  // per-wave group slots, or (ROT) all of x_i8: token t at t * (K + 16)
+  __shared__ __attribute__((aligned(1024))) int8_t xs[ROT ? kRotXBytes : kRowsMaxWaves * P * kXSlot];
+  __shared__ float rot_buf[ROT ? kRowsMaxWaves * rot::kWaveBufWords : 1];  // rotation transposes
+  __shared__ unsigned tok_max[kRotMaxM];  // ROT: absmax bits of each token
   __shared__ float row_scale[32];        // a_scale of the tokens
   __shared__ float col_scale[32 * NS];   // smax of the rows
   typedef int v16i __attribute__((ext_vector_type(16)));
@@ -439,6 +464,7 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
   const int R = r1 - r0;  // 1 .. 32 NS (checked by the planner)
 
   for (int i = threadIdx.x; i < 32 * NS * kRedStride; i += blockDim.x) red[i] = 0;
+  if (ROT && threadIdx.x < kRotMaxM) tok_max[threadIdx.x] = 0u;
   __syncthreads();
 
   const int g0 = (wave * G) / nw;
@@ -451,7 +477,7 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
   const bool scale_wave = wave == nw - 1 && a.out_kind != kOutAcc;
   float sc_row = 0.0f, sc_col0 = 0.0f, sc_col1 = 0.0f;
   if (scale_wave) {
-    sc_row = a.a_scale[min(lane, M - 1)];
+    if (!ROT) sc_row = a.a_scale[min(lane, M - 1)];
     sc_col0 = a.smax[r0 + min(lane, R - 1)];
     sc_col1 = a.smax[r0 + min(lane + 64, R - 1)];
   }
@@ -465,6 +491,25 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
     for (int s = 0; s < NS; ++s) {
       const int n = min(r0 + 32 * s + j, r1 - 1);
       wbase[s] = static_cast<size_t>(n >> 6) * G * 2048 + (n & 63) * 32 + h * 16;
+    }
+    // ROT: this wave's blocks of x (block bi = wave + i nw of the M x K/1024
+    // blocks is token bi / nblk, block bi % nblk), loaded first: waits complete
+    // in issue order, so behind the q and weight loads the rotation would wait
+    // for those too
+    const int nblk = K >> 10;
+    const int nbt = ROT ? M * nblk : 0;  // <= kRotBlocksPerWave * nw (checked by the host)
+    rot::BlockIn rin[ROT ? kRotBlocksPerWave : 1];
+    if (ROT) {
+      // no branch around the loads (a join with loads in flight makes the
+      // compiler wait for them): slots past the last block re-load it
+#pragma unroll
+      for (int i = 0; i < kRotBlocksPerWave; ++i) {
+        const int bi = min(wave + i * nw, nbt - 1);
+        const int t = bi / nblk, b = bi - t * nblk;
+        rin[i] = rot::load_block_rt(a.xb + static_cast<size_t>(t) * (a.silu ? 2 * K : K), a.sign,
+                                    a.silu ? K : 0, b, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // all of them ahead of the q and weight loads
     }
     // q of this lane's rows for all of the wave's groups: QD dwords from the
     // 4-aligned start q[n, g0 & ~3] (rows of q are G bytes, G % 8 == 0, so no
@@ -525,12 +570,61 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
             reinterpret_cast<const u32x4*>(a.packed + wbase[s] + static_cast<size_t>(g) * 2048));
         d.w[s] = make_uint4(t.x, t.y, t.z, t.w);
       }
-      const uint32_t slot = __builtin_amdgcn_readfirstlane(xs_wave + (jj % P) * kXSlot);
-      const uint32_t gx = static_cast<uint32_t>(g) * 128;
-      dma16xn(xi, xbase, xoff[0] + gx, xoff[1] + gx, xoff[2] + gx, slot, slot + 1024, slot + 2048);
+      if (!ROT) {
+        const uint32_t slot = __builtin_amdgcn_readfirstlane(xs_wave + (jj % P) * kXSlot);
+        const uint32_t gx = static_cast<uint32_t>(g) * 128;
+        dma16xn(xi, xbase, xoff[0] + gx, xoff[1] + gx, xoff[2] + gx, slot, slot + 1024, slot + 2048);
+      }
     };
 #pragma unroll
     for (int jj = 0; jj < P; ++jj) issue(buf[jj], jj);
+
+    if (ROT) {
+      // Every wave has groups here (the planner keeps nw <= G), so all of them
+      // reach the two barriers.
+      float* wb = rot_buf + wave * rot::kWaveBufWords;
+      float rv[kRotBlocksPerWave][16];
+#pragma unroll
+      for (int i = 0; i < kRotBlocksPerWave; ++i) {
+        const int bi = wave + i * nw;
+        if (bi < nbt) {
+          const int t = bi / nblk;
+          if (a.silu)
+            rot::rotate_loaded<true>(rin[i], lane, wb, rv[i]);
+          else
+            rot::rotate_loaded<false>(rin[i], lane, wb, rv[i]);
+          float m = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(rv[i][e]));
+#pragma unroll
+          for (int sh = 32; sh >= 1; sh >>= 1) m = fmaxf(m, __shfl_xor(m, sh));
+          // non-negative floats order like their bit patterns
+          if (lane == 0) atomicMax(&tok_max[t], __float_as_uint(m));
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kRotBlocksPerWave; ++i) {
+        const int bi = wave + i * nw;
+        if (bi < nbt) {
+          const int t = bi / nblk, b = bi - t * nblk;
+          const rot::TokenQuant tq = rot::token_quant(__uint_as_float(tok_max[t]));
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t word = rot::quant_run(rv[i], c, tq);
+            const int k = b * rot::kBlock + 256 * c + 4 * lane;
+            *reinterpret_cast<uint32_t*>(xs + t * (K + 16) + k) = word;
+            if (blockIdx.x == 0) *reinterpret_cast<uint32_t*>(a.x_i8_out + static_cast<size_t>(t) * K + k) = word;
+          }
+        }
+      }
+      if (wave == 0 && lane < M) {
+        const float sc = rot::token_quant(__uint_as_float(tok_max[lane])).scale;
+        row_scale[lane] = sc;
+        if (blockIdx.x == 0) a.a_scale_out[lane] = sc;
+      }
+      __syncthreads();
+    }
 
     v16i acc[NS];
 #pragma unroll
@@ -541,14 +635,21 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
       // this group's activation DMAs are done once at most the loads of the
       // groups issued after it are outstanding (NS + xi per group; counting
       // NS + 1 only makes the wait stricter)
-      wait_groups_after<NS + 1>(min(P - 1, GMAX - 1 - jj));
+      if (!ROT) wait_groups_after<NS + 1>(min(P - 1, GMAX - 1 - jj));
       asm volatile("" ::: "memory");
       if (jj == 0 || jj < ng) {
-        const int8_t* xr = xs + (wave * P + jj % P) * kXSlot + jr * 128;
         v4i xv[4];
+        if (ROT) {
+          // token min(j, M - 1), bytes 64 h .. 64 h + 63 of the group
+          const int8_t* xr = xs + min(j, M - 1) * (K + 16) + (g0 + min(jj, ng - 1)) * 128 + 64 * h;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          xv[t] = *reinterpret_cast<const v4i*>(xr + 16 * ((4 * h + t) ^ chunk_swizzle(jr)));
+          for (int t = 0; t < 4; ++t) xv[t] = *reinterpret_cast<const v4i*>(xr + 16 * t);
+        } else {
+          const int8_t* xr = xs + (wave * P + jj % P) * kXSlot + jr * 128;
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            xv[t] = *reinterpret_cast<const v4i*>(xr + 16 * ((4 * h + t) ^ chunk_swizzle(jr)));
+        }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const QTables tab = make_tables(qbyte(s, jj));
@@ -573,7 +674,7 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
     }
   }
   if (scale_wave) {
-    if (lane < M) row_scale[lane] = sc_row;
+    if (!ROT && lane < M) row_scale[lane] = sc_row;
     if (lane < R) col_scale[lane] = sc_col0;
     if (lane + 64 < R) col_scale[lane + 64] = sc_col1;
   }
@@ -721,7 +822,7 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceI
   return make_plan_for(M, N, K, dev, false);
 }
 
-template <int NS, int MAXT>
+template <int NS, int MAXT, bool ROT = false>
 hipError_t launch_rows_ns(GemvArgs a, int M, const GemvPlan& pl, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(pl.rows_wgs));
   const dim3 block(64 * pl.nw);
@@ -731,21 +832,26 @@ hipError_t launch_rows_ns(GemvArgs a, int M, const GemvPlan& pl, hipStream_t str
   // five in flight, most where N needs two rounds of workgroups).
   constexpr int PM = 5;
   switch (pl.gmax) {
-    case 3: hipLaunchKernelGGL((gemv_rows_kernel<NS, 3, 3, MAXT>), grid, block, 0, stream, a, M); break;
-    case 5: hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 2, MAXT>), grid, block, 0, stream, a, M); break;
-    case 9: hipLaunchKernelGGL((gemv_rows_kernel<NS, 9, PM, MAXT>), grid, block, 0, stream, a, M); break;
-    case 17: hipLaunchKernelGGL((gemv_rows_kernel<NS, 17, PM, MAXT>), grid, block, 0, stream, a, M); break;
-    case 33: hipLaunchKernelGGL((gemv_rows_kernel<NS, 33, PM, MAXT>), grid, block, 0, stream, a, M); break;
+    case 3: hipLaunchKernelGGL((gemv_rows_kernel<NS, 3, 3, MAXT, ROT>), grid, block, 0, stream, a, M); break;
+    case 5: hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 2, MAXT, ROT>), grid, block, 0, stream, a, M); break;
+    case 9: hipLaunchKernelGGL((gemv_rows_kernel<NS, 9, PM, MAXT, ROT>), grid, block, 0, stream, a, M); break;
+    case 17: hipLaunchKernelGGL((gemv_rows_kernel<NS, 17, PM, MAXT, ROT>), grid, block, 0, stream, a, M); break;
+    case 33:
+      // K > kRotMaxK: never planned with ROT
+      if (ROT) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemv_rows_kernel<NS, 33, PM, MAXT>), grid, block, 0, stream, a, M);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <bool ROT>
 hipError_t launch_rows(GemvArgs a, int M, const GemvPlan& pl, hipStream_t stream) {
   switch (pl.rows_ns) {
-    case 1: return launch_rows_ns<1, 512>(a, M, pl, stream);
-    case 2: return launch_rows_ns<2, 512>(a, M, pl, stream);
-    case 3: return launch_rows_ns<3, 512>(a, M, pl, stream);
+    case 1: return launch_rows_ns<1, 512, ROT>(a, M, pl, stream);
+    case 2: return launch_rows_ns<2, 512, ROT>(a, M, pl, stream);
+    case 3: return launch_rows_ns<3, 512, ROT>(a, M, pl, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -810,7 +916,7 @@ hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* 
                  pl.rows_ns > 0 ? "-rows" : (pl.mfma ? "-mfma" : ""), static_cast<long long>(M),
                  static_cast<long long>(N), static_cast<long long>(K), pl.gmax, pl.nw, pl.slices,
                  pl.rows_ns > 0 ? pl.rows_wgs : pl.n_rb * pl.slices);
-  GemvArgs a;
+  GemvArgs a = {};
   a.x = x_i8;
   a.a_scale = a_scale;
   a.packed = packed;
@@ -827,7 +933,7 @@ hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* 
   hipError_t e = hipErrorInvalidValue;
   if (pl.rows_ns > 0) {
     if (M > kXRows || pl.nw * 64 > 512) return hipErrorInvalidValue;  // x slots hold kXRows tokens
-    e = launch_rows(a, static_cast<int>(M), pl, stream);
+    e = launch_rows<false>(a, static_cast<int>(M), pl, stream);
   } else if (pl.mfma) {
     if (M > 32 || pl.nw * 64 > (pl.gmax <= 3 ? 1024 : 512)) return hipErrorInvalidValue;
     e = launch_mfma(a, static_cast<int>(M), pl, stream);
@@ -864,6 +970,48 @@ hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* 
   hipLaunchKernelGGL(gemv_reduce_kernel, dim3(blocks), dim3(256), 0, stream, a.part, pl.slices,
                      static_cast<int>(M), a.N, a_scale, smax, out, a.out_kind);
   return hipGetLastError();
+}
+
+
+// The fused decode kernel applies when the row-balanced plan does and the
+// whole rotation fits the workgroup: at most kRotMaxM tokens of at most
+// kRotMaxK, and at most kRotBlocksPerWave 1024-blocks per wave.
+bool gemv_rot_applies(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
+  if (M < 1 || M > kRotMaxM || K > kRotMaxK || N < 1) return false;
+  const GemvPlan pl = make_rows_plan(N, K, dev);
+  if (pl.slices <= 0 || pl.rows_ns <= 0 || pl.gmax > 17 || pl.nw * 64 > 512 || pl.nw > (K >> 7))
+    return false;
+  return M * (K >> 10) <= static_cast<int64_t>(kRotBlocksPerWave) * pl.nw;
+}
+
+hipError_t launch_gemv_rot(const uint16_t* x, const int8_t* sign, bool silu, const uint8_t* packed,
+                           const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
+                           void* out, OutKind out_kind, int8_t* x_i8, float* a_scale,
+                           const DeviceInfo& dev, hipStream_t stream) {
+  if (!gemv_rot_applies(M, N, K, dev)) return hipErrorNotSupported;
+  const GemvPlan pl = make_rows_plan(N, K, dev);
+  if (std::getenv("TWL_LOG"))
+    std::fprintf(stderr, "[twl] gemv-rows+rotation M=%lld N=%lld K=%lld silu=%d -> <= %d groups/wave, %d waves/WG, grid=%d\n",
+                 static_cast<long long>(M), static_cast<long long>(N), static_cast<long long>(K),
+                 silu ? 1 : 0, pl.gmax, pl.nw, pl.rows_wgs);
+  GemvArgs a = {};
+  a.a_scale = a_scale;
+  a.packed = packed;
+  a.q = q;
+  a.smax = smax;
+  a.out = out;
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  a.G = static_cast<int>(K >> 7);
+  a.n_rb = pl.n_rb;
+  a.slices = 1;
+  a.out_kind = out_kind;
+  a.xb = x;
+  a.sign = sign;
+  a.x_i8_out = x_i8;
+  a.a_scale_out = a_scale;
+  a.silu = silu ? 1 : 0;
+  return launch_rows<true>(a, static_cast<int>(M), pl, stream);
 }
 
 }  // namespace twl

@@ -72,4 +72,14 @@ size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, GemvKind kind, cons
 // The decode plan for this shape, as twl_plan_info reports it (info[0..7]).
 void gemv_plan_info(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceInfo& dev, int64_t* info);
 
+// Fused decode: rotate_quant_act (silu: of bf16(SiLU(gate) * up), x being
+// [gate | up] [M, 2K]) and the row-balanced decode kernel in one launch, which
+// also writes x_i8 [M, K] and a_scale [M].  gemv_rot_applies tells whether the
+// shape fits it; launch_gemv_rot returns hipErrorNotSupported otherwise.
+bool gemv_rot_applies(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev);
+hipError_t launch_gemv_rot(const uint16_t* x, const int8_t* sign, bool silu, const uint8_t* packed,
+                           const int8_t* q, const float* smax, int64_t M, int64_t N, int64_t K,
+                           void* out, OutKind out_kind, int8_t* x_i8, float* a_scale,
+                           const DeviceInfo& dev, hipStream_t stream);
+
 }  // namespace twl

@@ -45,6 +45,8 @@ hipError_t g_symbol_status = hipSuccess;
 int g_symbol_lookups = 0;
 alignas(256) unsigned char g_fake_scratch_mem[256];
 void* g_fake_scratch = g_fake_scratch_mem;
+// whether the fused rotation + decode kernel applies (stubbed planner)
+bool g_rot_applies = false;
 
 }  // namespace
 
@@ -97,7 +99,7 @@ hipError_t launch_reference_bf16(const uint16_t*, const uint8_t*, const uint16_t
 }
 hipError_t launch_silu_mul_rotate_quant(const uint16_t*, const int8_t*, int64_t M, int64_t K, int8_t*, float*,
                                         hipStream_t) {
-  return record(M, 0, K, -1, nullptr);
+  return record(M, 0, K, -2, nullptr);
 }
 hipError_t launch_pack(const int8_t*, const uint16_t*, int64_t N, int64_t K, uint8_t*, int8_t*, float*,
                        int32_t*, hipStream_t) {
@@ -124,6 +126,12 @@ size_t gemv_workspace_bytes(int64_t, int64_t, int64_t, GemvKind, const DeviceInf
 void gemv_plan_info(int64_t, int64_t, int64_t, GemvKind kind, const DeviceInfo&, int64_t* info) {
   for (int i = 0; i < 8; ++i) info[i] = 2000 + i;
   info[0] = 2 + kind;
+}
+bool gemv_rot_applies(int64_t, int64_t, int64_t, const DeviceInfo&) { return g_rot_applies; }
+hipError_t launch_gemv_rot(const uint16_t*, const int8_t*, bool silu, const uint8_t*, const int8_t*,
+                           const float*, int64_t M, int64_t N, int64_t K, void*, OutKind out_kind, int8_t*,
+                           float*, const DeviceInfo&, hipStream_t) {
+  return record(M, N, K, 300 + 10 * (silu ? 1 : 0) + out_kind, nullptr);
 }
 }  // namespace twl
 
@@ -300,6 +308,73 @@ void test_noalloc() {
   g_device = 0;
 }
 
+// twl_rotate_quant_linear: one fused launch when the (stubbed) planner allows
+// it, else the rotation and then the linear layer; every argument and the
+// workspace checked before anything is launched
+void test_rotate_quant_linear() {
+  auto* x = static_cast<const uint16_t*>(P);
+  auto* s8 = static_cast<const int8_t*>(P);
+  auto* u8 = static_cast<const uint8_t*>(P);
+  auto* f = static_cast<float*>(P);
+  auto* i8 = static_cast<int8_t*>(P);
+  const auto call = [&](int64_t M, int64_t N, int silu, int kind, void* ws, size_t ws_bytes) {
+    return twl_rotate_quant_linear(x, s8, u8, s8, f, M, N, 5120, silu, i8, f, P, kind, ws, ws_bytes, nullptr);
+  };
+  g_device = 0;
+  g_launch_status = hipSuccess;
+  g_gemm_ws = g_gemv_ws = 0;
+
+  // fused: one launch, with the silu flag and the output kind
+  g_rot_applies = true;
+  int before = g_launches;
+  CHECK(call(1, 17408, 0, TWL_OUT_F32, nullptr, 0) == TWL_OK);
+  CHECK(g_launches == before + 1 && g_last_kind == 300 + TWL_OUT_F32 && g_last_m == 1 && g_last_n == 17408);
+  CHECK(call(2, 17408, 1, TWL_OUT_BF16, nullptr, 0) == TWL_OK);
+  CHECK(g_launches == before + 2 && g_last_kind == 310 + TWL_OUT_BF16);
+  CHECK(twl_rotate_quant_linear_fused(1, 17408, 5120) == 1);
+  CHECK(twl_rotate_quant_linear_fused(0, 17408, 5120) == 0);
+  CHECK(twl_rotate_quant_linear_fused(1, 17408, 1000) == -TWL_ESHAPE);
+
+  // two steps: the rotation (plain or SiLU form), then the decode or GEMM path
+  g_rot_applies = false;
+  before = g_launches;
+  CHECK(call(4, 17408, 0, TWL_OUT_F32, nullptr, 0) == TWL_OK);
+  CHECK(g_launches == before + 2 && g_last_kind == 200 + 10 * twl::kGemvAuto + TWL_OUT_F32);
+  CHECK(call(100, 17408, 1, TWL_OUT_ACC_I32, nullptr, 0) == TWL_OK);
+  CHECK(g_launches == before + 4 && g_last_kind == 100 + TWL_OUT_ACC_I32);
+  CHECK(twl_rotate_quant_linear_fused(4, 17408, 5120) == 0);
+  // N = 0: the rotation alone
+  CHECK(call(4, 0, 1, TWL_OUT_F32, nullptr, 0) == TWL_OK);
+  CHECK(g_launches == before + 5 && g_last_kind == -2);
+
+  // a missing workspace is refused before the rotation is enqueued
+  g_gemm_ws = 4096;
+  before = g_launches;
+  CHECK(call(100, 17408, 0, TWL_OUT_F32, nullptr, 0) == TWL_EINVAL && msg_has("workspace"));
+  CHECK(call(100, 17408, 0, TWL_OUT_F32, P2, 4096) == TWL_EALIGN);
+  CHECK(g_launches == before);
+  CHECK(call(100, 17408, 0, TWL_OUT_F32, P, 4096) == TWL_OK);
+  CHECK(g_launches == before + 2 && g_last_ws == P);
+  g_gemm_ws = 0;
+
+  // a failing launch maps to TWL_EHIP, naming the step; after a failed
+  // rotation nothing else is launched
+  g_launch_status = hipErrorLaunchFailure;
+  g_rot_applies = true;
+  CHECK(call(1, 17408, 0, TWL_OUT_F32, nullptr, 0) == TWL_EHIP && msg_has("fused decode"));
+  g_rot_applies = false;
+  before = g_launches;
+  CHECK(call(4, 17408, 0, TWL_OUT_F32, nullptr, 0) == TWL_EHIP && msg_has("rotation"));
+  CHECK(g_launches == before + 1);
+  g_launch_status = hipSuccess;
+
+  // a device that is not gfx950
+  g_device = 1;
+  CHECK(call(1, 17408, 0, TWL_OUT_F32, nullptr, 0) == TWL_EDEVICE);
+  CHECK(twl_rotate_quant_linear_fused(1, 17408, 5120) == -TWL_EDEVICE);
+  g_device = 0;
+}
+
 }  // namespace
 
 int main() {
@@ -307,6 +382,7 @@ int main() {
   test_status_mapping();
   test_dispatch_and_workspace();
   test_noalloc();
+  test_rotate_quant_linear();
   if (g_failures == 0) std::printf("abi_driver: all checks passed\n");
   return g_failures == 0 ? 0 : 1;
 }

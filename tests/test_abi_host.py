@@ -72,6 +72,37 @@ def test_fused_activation_rejects_bad_args(lib):
     assert f(None, None, 0, 1024, None, None, None) == 0
 
 
+def test_rotate_quant_linear_rejects_bad_args(lib):
+    f = lib.twl_rotate_quant_linear
+    P = FAKE
+
+    def call(x=P, sign=P, packed=P, q=P, smax=P, M=4, N=64, K=1024, silu=0, x_i8=P, a_scale=P,
+             out=P, kind=0):
+        return f(x, sign, packed, q, smax, M, N, K, silu, x_i8, a_scale, out, kind, None, 0, None)
+
+    assert call(K=1000) == 2 and b"K=" in lib.twl_last_error()
+    assert call(silu=2) == 1 and b"silu" in lib.twl_last_error()
+    assert call(kind=5) == 1
+    assert call(M=-1) == 1
+    assert call(x=None) == 1 and b"x is NULL" in lib.twl_last_error()
+    assert call(sign=P + 2) == 3
+    assert call(x_i8=None) == 1
+    assert call(a_scale=None) == 1
+    assert call(packed=None) == 1 and b"packed is NULL" in lib.twl_last_error()
+    assert call(out=None) == 1
+    assert call(smax=None) == 1
+    # M = 0 is a no-op; N = 0 needs only the rotation's buffers (it then fails
+    # later, on the device query, which this host has not: not a validation error)
+    assert call(x=None, sign=None, packed=None, q=None, smax=None, M=0, x_i8=None, a_scale=None,
+                out=None) == 0
+    assert call(packed=None, q=None, smax=None, out=None, N=0) not in (1, 2, 3)
+    # the raw accumulators need no smax
+    assert call(smax=None, kind=1) not in (1, 2, 3)
+    fused = lib.twl_rotate_quant_linear_fused
+    assert fused(4, 64, 1000) == -2
+    assert fused(-1, 64, 1024) == -1
+
+
 def test_pack_rejects_bad_args(lib):
     assert lib.twl_pack_ternary(FAKE, FAKE, 8, 1000, FAKE, FAKE, FAKE, None, None) == 2
     assert lib.twl_pack_ternary(FAKE, None, 8, 1024, FAKE, FAKE, FAKE, None, None) == 1

@@ -56,8 +56,13 @@ def test_m0_only_feeds_our_lds_loads(tmp_path_factory, asm, src):
     kernel, least = M0_KERNELS[src]
     kernels = _kernels(text, kernel, least)
     for name, body in kernels.items():
-        assert "global_load_lds" in body, name
         lines = [ln.strip() for ln in body.splitlines() if ln.strip() and not ln.strip().startswith(";")]
+        if src == "gemv.hip" and "ELb1EEEv" in name:
+            # the fused-rotation decode kernels quantise x into LDS themselves:
+            # no direct loads, and so no M0 at all
+            assert not any("global_load_lds" in ln or "m0" in ln for ln in lines), name
+            continue
+        assert "global_load_lds" in body, name
         for i, ln in enumerate(lines):
             if "m0" not in ln:
                 continue

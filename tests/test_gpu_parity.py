@@ -518,3 +518,77 @@ def test_plan_info_matches_workspace_and_family(twl, M, N, K, path, family):
     assert plan["reduce_kernel"] == (1 if plan["splits"] > 1 else 0)
     assert plan["workspace_bytes"] <= twl.workspace_bytes(M, N, K)
     assert (plan["workspace_bytes"] > 0) == (plan["splits"] > 1)
+
+
+# ------------- rotate_quant_linear: the layer from bf16 x, fused at small M
+
+@pytest.mark.parametrize("M,N,K,silu,fused", [
+    (1, 17408, 5120, False, True),   # decode gate/up: 5 blocks over 8 waves
+    (4, 17408, 5120, False, True),   # 20 blocks
+    (3, 17408, 5120, True, True),    # the SiLU form
+    (1, 5120, 17408, True, True),    # decode down with its SiLU input: 17 blocks
+    (1, 5120, 17408, False, True),
+    (2, 24577, 1024, False, True),   # two rounds of workgroups, ragged rows
+    (1, 8000, 9216, True, True),     # one 32-row subtile, 9 groups per wave
+    (2, 5120, 17408, False, False),  # 34 blocks: more than 3 per wave, two steps
+    (5, 17408, 5120, False, False),  # more than 4 tokens
+    (64, 2048, 2048, True, False),   # prefill: the GEMM path
+])
+def test_rotate_quant_linear(twl, M, N, K, silu, fused):
+    layer = W.make_layer(7000 + M + N + K, M, K, N)
+    if silu:
+        xin, sign = W.make_gate_up(7100 + M + K, M, K)
+        ox, osc = O.silu_mul_rotate_quant_act(xin, sign)
+    else:
+        xin, sign = layer.x_bits.copy(), layer.sign
+        if M >= 3:
+            xin[1] = 0  # an all-zero token: a_scale 0, x_i8 0
+        ox, osc = O.rotate_quant_act(xin, sign)
+    packed, q, smax = gpu_pack(twl, layer.code, layer.s_bits)
+    oq, osm = O.decompose_scales(layer.s_bits)
+    assert twl.rotate_quant_linear_fused(M, N, K) == fused
+    announce(f"rotate_quant_linear M={M} N={N} K={K} silu={silu} fused={fused}")
+    x, sg = dev(xin.view(np.int16)), dev(sign)
+    y, xi, sc = twl.rotate_quant_linear(x, sg, packed, q, smax, silu=silu)
+    acc = twl.rotate_quant_linear(x, sg, packed, q, smax, silu=silu, out_dtype=torch.int32)[0]
+    yb = twl.rotate_quant_linear(x, sg, packed, q, smax, silu=silu, out_dtype=torch.bfloat16)[0]
+    assert np.array_equal(host(sc).view(np.uint32), osc.view(np.uint32)), "a_scale differs"
+    bad = np.argwhere(host(xi) != ox)
+    assert bad.size == 0, f"{len(bad)} x_i8 mismatches, first {bad[:5].tolist()}"
+    oacc = O.linear_acc(ox, layer.code, oq)
+    bad = np.argwhere(host(acc) != oacc)
+    assert bad.size == 0, f"{len(bad)} acc mismatches, first {bad[:5].tolist()}"
+    np.testing.assert_allclose(host(y), O.epilogue(oacc, osc, osm), rtol=Y_RTOL, atol=0)
+    # bit for bit what the two calls give
+    rot = twl.silu_mul_rotate_quant_act if silu else twl.rotate_quant_act
+    xi2, sc2 = rot(x, sg)
+    assert torch.equal(y, twl.ternary_linear(xi2, sc2, packed, q, smax))
+    assert torch.equal(yb, twl.ternary_linear_bf16(xi2, sc2, packed, q, smax))
+
+
+def test_rotate_quant_linear_graph_replays(twl):
+    # the fused kernel captured in a HIP graph: every replay equals the eager call
+    M, N, K = 2, 17408, 5120
+    layer = W.make_layer(7300, M, K, N)
+    packed, q, smax = gpu_pack(twl, layer.code, layer.s_bits)
+    assert twl.rotate_quant_linear_fused(M, N, K)
+    x, sg = dev(layer.x_bits.view(np.int16)), dev(layer.sign)
+    announce("rotate_quant_linear graph replays")
+    y0 = twl.rotate_quant_linear(x, sg, packed, q, smax)[0].clone()
+    y = torch.empty_like(y0)
+    xi = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    sc = torch.empty((M,), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        twl.rotate_quant_linear(x, sg, packed, q, smax, out=y, x_i8=xi, a_scale=sc)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        twl.rotate_quant_linear(x, sg, packed, q, smax, out=y, x_i8=xi, a_scale=sc)
+    for _ in range(3):
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0)
