@@ -61,7 +61,7 @@ typedef enum {
   TWL_PATH_GEMM = 1,       /* int8-MFMA GEMM with in-register 2-bit unpack         */
   TWL_PATH_GEMV = 2,       /* decode kernel (M <= TWL_GEMV_MAX_M), chosen by shape */
   TWL_PATH_GEMV_DOT4 = 3,  /* decode: packed-2-bit dot4 GEMV, no matrix cores      */
-  TWL_PATH_GEMV_MFMA = 4   /* decode: 32-token-padded int8 MFMA over the stream    */
+  TWL_PATH_GEMV_MFMA = 4   /* decode: int8 MFMA over the stream (tokens padded to 16 or 32) */
 } twl_path;
 
 /*
@@ -147,9 +147,10 @@ size_t twl_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   acc[t,n] = sum_k x_i8[t,k] * code[n,k] * q[n, k/128]      (exact int32)
  *   y[t,n]   = acc[t,n] * a_scale[t] * smax[n] / 127           (fp32)
  *   Prefill sizes run an int8-MFMA GEMM that unpacks the 2-bit codes on chip;
- *   decode batches (M <= TWL_GEMV_MAX_M) stream the packed weights through a
- *   32-token-padded int8 MFMA kernel (every CU an equal range of rows when
- *   each CU gets at least 16 rows) or, for narrower layers, a dot4 GEMV
+ *   decode batches (M <= TWL_GEMV_MAX_M) stream the packed weights through an
+ *   int8 MFMA kernel, tokens padded to 16 (M <= 16) or 32 (every CU an equal
+ *   range of rows when each CU gets at least 16 rows) or, for narrower
+ *   layers, a dot4 GEMV
  *   (M < 4) or a K-split MFMA kernel.  All give
  *   bit-identical acc.
  *   x_i8 [M,K], a_scale [M], packed (twl_packed_bytes(N,K) bytes), q [N,K/128],
@@ -273,9 +274,9 @@ twl_status twl_plan_info(int64_t M, int64_t N, int64_t K, int path, int64_t* inf
  *   x_i8      out: int8 [M, K];  a_scale out: fp32 [M]  (device, caller-owned)
  *   out       out: [M, N] of the out_kind (twl_out)
  *   workspace     : as ternary_linear_ex for this M, N, K (twl_workspace_bytes)
- * For small decode batches (at most 4 tokens, K <= 17408, at most 3 1024-blocks
- * of rotation per wave of a decode workgroup, on shapes where the row-balanced
- * decode kernel applies) one fused kernel does both steps: every decode
+ * For small decode batches (at most 4 tokens, K <= 17408, at most 2 1024-blocks
+ * of rotation per wave of a decode workgroup, 3 for a single token, on shapes
+ * where the row-balanced decode kernel applies) one fused kernel does both steps: every decode
  * workgroup rotates and quantises the tokens itself while its first weight
  * loads are in flight, which removes the rotation's own launch from the
  * decode step.  Other shapes run the two kernels back to back on `stream`.

@@ -32,8 +32,9 @@
 //   Its VALU work grows with M: it is used for M < 4 on layers too narrow
 //   for the row-balanced kernel.
 // MFMA kernels: the tokens padded to 32 form the B operand of
-//   v_mfma_i32_32x32x32_i8 and the unpacked weights the A operand, which makes
-//   the work nearly independent of M.  gemv_rows_kernel gives every CU an
+//   v_mfma_i32_32x32x32_i8 (in gemv_rows_kernel at up to 16 tokens: padded to
+//   16, v_mfma_i32_16x16x64_i8) and the unpacked weights the A operand, which
+//   makes the work nearly independent of M.  gemv_rows_kernel gives every CU an
 //   equal contiguous range of rows over all of K (no partial sums leave the
 //   workgroup) and is used at every M whenever each CU gets at least 16 rows;
 //   gemv_mfma_kernel keeps the 64-row-block split with K slices (4 <= M <= 24)
@@ -41,6 +42,7 @@
 #include "rotate_block.h"
 
 #include <algorithm>
+#include <type_traits>
 #include <cstdio>
 #include <cstdlib>
 
@@ -56,6 +58,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(4))) const u32x4 const_u32x4;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i_t __attribute__((ext_vector_type(16)));
 
 // The 16 int8 weights {code * q} of one packed word (16 codes), as the four
 // dwords of a dot4 operand (dword i = codes 4i .. 4i+3 of the word).  Fields
@@ -405,15 +408,23 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(GemvArgs a, int M) {
 
 // Row-balanced matrix-core decode (M <= 24 tokens, N >= 16 rows per CU).
 // Streaming is bound per CU, so each workgroup takes an equal contiguous range
-// of rows [r0, r1) (any length up to 32 NS) over the whole of K: every CU
+// of rows [r0, r1) (any length up to RS NS) over the whole of K: every CU
 // streams the same number of bytes and no partial sums leave the workgroup.
-// The rows form NS subtiles of 32 (the A operand of v_mfma_i32_32x32x32_i8;
-// rows past r1 are computed and dropped).  The waves split K into runs of at
+// The rows form NS subtiles of RS rows, the A operand of the MFMA (rows past
+// r1 are computed and dropped):
+//   RS = 32 (17..24 tokens): v_mfma_i32_32x32x32_i8, lane (j, h) = (row or
+//     token j = lane % 32, half h = lane / 32); per 128-k group a lane holds
+//     16 packed bytes of its row (k = 64 h .. 64 h + 63), four MFMAs;
+//   RS = 16 (up to 16 tokens): v_mfma_i32_16x16x64_i8, lane (j, h) = (row or
+//     token j = lane % 16, quarter h = lane / 16); per group a lane holds 8
+//     packed bytes (k = 32 h .. 32 h + 31), two MFMAs.  Tokens pad to 16
+//     instead of 32 and rows to a multiple of 16.
+// Integer sums are exact, so A and B only have to agree on which k each
+// (lane group, byte) covers.  The waves split K into runs of at
 // most GMAX groups and keep P groups of loads in flight: group jj + P is issued
 // as soon as group jj has been consumed, so the stream and the unpack / MFMA
 // work overlap.  Loads are issued unconditionally (slots past the wave's run
 // re-read its last group) so that the compiler's vmcnt waits stay static.
-// Lane (j, h) layout as in gemv_mfma_kernel.
 // The activations of a group (at most kXRows tokens x 128 bytes) go to LDS
 // by direct loads with 8 lanes per 128-byte row, so each 1 KB load touches 16
 // cache lines; read as MFMA operands (16 bytes of one token per lane) they
@@ -430,10 +441,18 @@ constexpr int kRotMaxM = 4;
 constexpr int kRotMaxK = 17408;
 constexpr int kRotBlocksPerWave = 3;
 constexpr int kRotXBytes = kRotMaxM * (kRotMaxK + 16);
+// Up to this many tokens the row-balanced kernel uses 16-row subtiles and
+// v_mfma_i32_16x16x64_i8 (the tokens are one 16-wide operand); above, 32-row
+// subtiles and v_mfma_i32_32x32x32_i8.  Measured 0.1-0.7 us faster per call
+// on the decode layers at M = 1, 8 and 16 (5120 -> 17408: 8.62 -> 8.48 us at
+// M = 1, 11.10 -> 10.60 at M = 16; 17408 -> 5120: 10.50 -> 9.76 at M = 1).
+constexpr int kRows16MaxM = 16;
 
-template <int NS>
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+template <int NS, int RS>
 struct RowGroup {
-  uint4 w[NS];   // 16 packed bytes of row 32 s + j, half h
+  // RS = 32: 16 packed bytes of row 32 s + j, half h; RS = 16: 8 bytes of row 16 s + j, quarter h
+  typename std::conditional<RS == 32, uint4, uint2>::type w[NS];
 };
 
 // ROT: the workgroup first rotates and quantises the M <= kRotMaxM tokens
@@ -442,18 +461,19 @@ struct RowGroup {
 // stays in LDS for the whole K and no activation is loaded per group.  The
 // rotation and the quantiser are those of rotate_quant_act (rotate_block.h),
 // so x_i8, a_scale and y equal the two-step result bit for bit.
-template <int NS, int GMAX, int P, int MAXT, bool ROT = false>
+template <int NS, int GMAX, int P, int MAXT, bool ROT = false, int RS = 32>
 __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
   static_assert(P >= 1 && P <= GMAX, "prefetch depth");
   static_assert(MAXT <= 64 * kRowsMaxWaves, "x slots are sized for 8 waves");
-  __shared__ int red[32 * NS * kRedStride];
+  static_assert(RS == 32 || RS == 16, "subtile rows");
+  typedef typename std::conditional<RS == 32, v16i_t, v4i>::type acc_t;
+  __shared__ int red[RS * NS * kRedStride];
   // per-wave group slots, or (ROT) all of x_i8: token t at t * (K + 16)
   __shared__ __attribute__((aligned(1024))) int8_t xs[ROT ? kRotXBytes : kRowsMaxWaves * P * kXSlot];
   __shared__ float rot_buf[ROT ? kRowsMaxWaves * rot::kWaveBufWords : 1];  // rotation transposes
   __shared__ unsigned tok_max[kRotMaxM];  // ROT: absmax bits of each token
   __shared__ float row_scale[32];        // a_scale of the tokens
-  __shared__ float col_scale[32 * NS];   // smax of the rows
-  typedef int v16i __attribute__((ext_vector_type(16)));
+  __shared__ float col_scale[RS * NS];   // smax of the rows
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
@@ -463,7 +483,7 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
   const int r1 = static_cast<int>((static_cast<int64_t>(blockIdx.x + 1) * N) / gridDim.x);
   const int R = r1 - r0;  // 1 .. 32 NS (checked by the planner)
 
-  for (int i = threadIdx.x; i < 32 * NS * kRedStride; i += blockDim.x) red[i] = 0;
+  for (int i = threadIdx.x; i < RS * NS * kRedStride; i += blockDim.x) red[i] = 0;
   if (ROT && threadIdx.x < kRotMaxM) tok_max[threadIdx.x] = 0u;
   __syncthreads();
 
@@ -483,14 +503,14 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
   }
 
   if (ng > 0) {
-    const int j = lane & 31, h = lane >> 5;
+    const int j = lane & (RS - 1), h = lane / RS;
     // lanes past the last row of this workgroup re-read that row: the same
     // cache lines, so no bytes beyond the workgroup's own rows are fetched
     size_t wbase[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int n = min(r0 + 32 * s + j, r1 - 1);
-      wbase[s] = static_cast<size_t>(n >> 6) * G * 2048 + (n & 63) * 32 + h * 16;
+      const int n = min(r0 + RS * s + j, r1 - 1);
+      wbase[s] = static_cast<size_t>(n >> 6) * G * 2048 + (n & 63) * 32 + h * (RS == 32 ? 16 : 8);
     }
     // ROT: this wave's blocks of x (block bi = wave + i nw of the M x K/1024
     // blocks is token bi / nblk, block bi % nblk), loaded first: waits complete
@@ -523,23 +543,20 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
     typedef uint32_t qvec __attribute__((ext_vector_type(QV)));
     const int qa = g0 & ~3, qsh = g0 & 3;
     const int qd_last = (G - qa) / 4 - 1;
-    qvec qw0 = {}, qw1 = {}, qw2 = {};
+    qvec qw[NS];  // indexed by constants only (unrolled), so kept in registers
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int n = min(r0 + 32 * s + j, r1 - 1);
+      const int n = min(r0 + RS * s + j, r1 - 1);
       const uint32_t* qrow = reinterpret_cast<const uint32_t*>(a.q + static_cast<size_t>(n) * G + qa);
       qvec v = {};
 #pragma unroll
       for (int d = 0; d < QD; ++d) v[d] = qrow[min(d, qd_last)];
-      if (s == 0) qw0 = v;
-      else if (s == 1) qw1 = v;
-      else qw2 = v;
+      qw[s] = v;
     }
-    static_assert(NS <= 3, "q vectors for at most 3 subtiles");
     // q[n, g0 + jj]: byte qsh + jj of the run (jj is a constant once unrolled):
     // a 64-bit shift of two dwords picked by constant indices
     const auto qbyte = [&](int s, int jj) {
-      const qvec& v = s == 0 ? qw0 : (s == 1 ? qw1 : qw2);
+      const qvec& v = qw[s];
       const uint64_t w = (static_cast<uint64_t>(v[(jj >> 2) + 1]) << 32) | v[jj >> 2];
       return static_cast<int>(static_cast<int8_t>(w >> (8 * (qsh + (jj & 3)))));
     };
@@ -561,14 +578,20 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
     // per group: NS weight loads (VGPR), then the xi activation DMAs; the
     // activation wait below counts on exactly this order.  The weights are
     // read once per call: nontemporal loads (measured 2-3% faster)
-    RowGroup<NS> buf[P];
-    auto issue = [&](RowGroup<NS>& d, int jj) {
+    RowGroup<NS, RS> buf[P];
+    auto issue = [&](RowGroup<NS, RS>& d, int jj) {
       const int g = g0 + min(jj, ng - 1);
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const u32x4 t = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(a.packed + wbase[s] + static_cast<size_t>(g) * 2048));
-        d.w[s] = make_uint4(t.x, t.y, t.z, t.w);
+        if constexpr (RS == 32) {
+          const u32x4 t = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(a.packed + wbase[s] + static_cast<size_t>(g) * 2048));
+          d.w[s] = make_uint4(t.x, t.y, t.z, t.w);
+        } else {
+          const u32x2 t = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x2*>(a.packed + wbase[s] + static_cast<size_t>(g) * 2048));
+          d.w[s] = make_uint2(t.x, t.y);
+        }
       }
       if (!ROT) {
         const uint32_t slot = __builtin_amdgcn_readfirstlane(xs_wave + (jj % P) * kXSlot);
@@ -626,37 +649,46 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
       __syncthreads();
     }
 
-    v16i acc[NS];
+    acc_t acc[NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) acc[s] = v16i{0};
+    for (int s = 0; s < NS; ++s) acc[s] = acc_t{0};
 #pragma unroll
     for (int jj = 0; jj < GMAX; ++jj) {
-      RowGroup<NS>& d = buf[jj % P];
+      RowGroup<NS, RS>& d = buf[jj % P];
       // this group's activation DMAs are done once at most the loads of the
       // groups issued after it are outstanding (NS + xi per group; counting
       // NS + 1 only makes the wait stricter)
       if (!ROT) wait_groups_after<NS + 1>(min(P - 1, GMAX - 1 - jj));
       asm volatile("" ::: "memory");
       if (jj == 0 || jj < ng) {
-        v4i xv[4];
+        // k-chunks (16 bytes) of the group this lane supplies: RS = 32, chunk
+        // 4 h + t for MFMA t = 0..3; RS = 16, chunk 2 h + t for MFMA t = 0, 1
+        constexpr int NT = RS == 32 ? 4 : 2;
+        v4i xv[NT];
         if (ROT) {
-          // token min(j, M - 1), bytes 64 h .. 64 h + 63 of the group
-          const int8_t* xr = xs + min(j, M - 1) * (K + 16) + (g0 + min(jj, ng - 1)) * 128 + 64 * h;
+          const int8_t* xr = xs + min(j, M - 1) * (K + 16) + (g0 + min(jj, ng - 1)) * 128 + 16 * NT * h;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) xv[t] = *reinterpret_cast<const v4i*>(xr + 16 * t);
+          for (int t = 0; t < NT; ++t) xv[t] = *reinterpret_cast<const v4i*>(xr + 16 * t);
         } else {
           const int8_t* xr = xs + (wave * P + jj % P) * kXSlot + jr * 128;
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            xv[t] = *reinterpret_cast<const v4i*>(xr + 16 * ((4 * h + t) ^ chunk_swizzle(jr)));
+          for (int t = 0; t < NT; ++t)
+            xv[t] = *reinterpret_cast<const v4i*>(xr + 16 * ((NT * h + t) ^ chunk_swizzle(jr)));
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const QTables tab = make_tables(qbyte(s, jj));
-          const uint32_t wv[4] = {d.w[s].x, d.w[s].y, d.w[s].z, d.w[s].w};
+          if constexpr (RS == 32) {
+            const uint32_t wv[4] = {d.w[s].x, d.w[s].y, d.w[s].z, d.w[s].w};
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            acc[s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(wv[t], tab), xv[t], acc[s], 0, 0, 0);
+            for (int t = 0; t < 4; ++t)
+              acc[s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(unpack16(wv[t], tab), xv[t], acc[s], 0, 0, 0);
+          } else {
+            const uint32_t wv[2] = {d.w[s].x, d.w[s].y};
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+              acc[s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(wv[t], tab), xv[t], acc[s], 0, 0, 0);
+          }
         }
       }
       if (jj + P < GMAX) issue(d, jj + P);
@@ -667,8 +699,9 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 32 * s + 8 * (r >> 2) + 4 * h + (r & 3);
+        for (int r = 0; r < (RS == 32 ? 16 : 4); ++r) {
+          // RS = 32: register r holds row 8 (r / 4) + 4 h + (r % 4); RS = 16: row 4 h + r
+          const int row = RS * s + (RS == 32 ? 8 * (r >> 2) + 4 * h + (r & 3) : 4 * h + r);
           atomicAdd(&red[row * kRedStride + j], acc[s][r]);
         }
     }
@@ -719,7 +752,8 @@ struct GemvPlan {
   int n_rb = 1;
   bool mfma = false;
   // row-balanced MFMA kernel: `rows_wgs` workgroups of an even share of N
-  int rows_ns = 0;   // 32-row subtiles per workgroup (0: not this kernel)
+  int rows_ns = 0;   // subtiles of rows_rs rows per workgroup (0: not this kernel)
+  int rows_rs = 32;
   int rows_wgs = 0;
 };
 
@@ -811,7 +845,14 @@ GemvPlan make_rows_plan(int64_t N, int64_t K, const DeviceInfo& dev) {
 // K-split matrix-core kernel from there on.
 GemvPlan make_plan(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceInfo& dev) {
   if (kind != kGemvDot4 && M <= kXRows) {
-    const GemvPlan r = make_rows_plan(N, K, dev);
+    GemvPlan r = make_rows_plan(N, K, dev);
+    if (r.slices > 0 && M <= kRows16MaxM) {
+      // 16-row subtiles and v_mfma_i32_16x16x64_i8: tokens padded to 16, not
+      // 32, and the rows of a workgroup to a multiple of 16
+      const int64_t rmax = (N + r.rows_wgs - 1) / r.rows_wgs;
+      r.rows_rs = 16;
+      r.rows_ns = static_cast<int>((rmax + 15) / 16);
+    }
     if (r.slices > 0) return r;
   }
   const bool want_mfma = kind == kGemvMfma || (kind == kGemvAuto && M >= kMfmaMinM);
@@ -822,7 +863,7 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceI
   return make_plan_for(M, N, K, dev, false);
 }
 
-template <int NS, int MAXT, bool ROT = false>
+template <int NS, int MAXT, bool ROT = false, int RS = 32>
 hipError_t launch_rows_ns(GemvArgs a, int M, const GemvPlan& pl, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(pl.rows_wgs));
   const dim3 block(64 * pl.nw);
@@ -832,14 +873,14 @@ hipError_t launch_rows_ns(GemvArgs a, int M, const GemvPlan& pl, hipStream_t str
   // five in flight, most where N needs two rounds of workgroups).
   constexpr int PM = 5;
   switch (pl.gmax) {
-    case 3: hipLaunchKernelGGL((gemv_rows_kernel<NS, 3, 3, MAXT, ROT>), grid, block, 0, stream, a, M); break;
-    case 5: hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 2, MAXT, ROT>), grid, block, 0, stream, a, M); break;
-    case 9: hipLaunchKernelGGL((gemv_rows_kernel<NS, 9, PM, MAXT, ROT>), grid, block, 0, stream, a, M); break;
-    case 17: hipLaunchKernelGGL((gemv_rows_kernel<NS, 17, PM, MAXT, ROT>), grid, block, 0, stream, a, M); break;
+    case 3: hipLaunchKernelGGL((gemv_rows_kernel<NS, 3, 3, MAXT, ROT, RS>), grid, block, 0, stream, a, M); break;
+    case 5: hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 2, MAXT, ROT, RS>), grid, block, 0, stream, a, M); break;
+    case 9: hipLaunchKernelGGL((gemv_rows_kernel<NS, 9, PM, MAXT, ROT, RS>), grid, block, 0, stream, a, M); break;
+    case 17: hipLaunchKernelGGL((gemv_rows_kernel<NS, 17, PM, MAXT, ROT, RS>), grid, block, 0, stream, a, M); break;
     case 33:
       // K > kRotMaxK: never planned with ROT
       if (ROT) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((gemv_rows_kernel<NS, 33, PM, MAXT>), grid, block, 0, stream, a, M);
+      hipLaunchKernelGGL((gemv_rows_kernel<NS, 33, PM, MAXT, false, RS>), grid, block, 0, stream, a, M);
       break;
     default: return hipErrorInvalidValue;
   }
@@ -848,6 +889,18 @@ hipError_t launch_rows_ns(GemvArgs a, int M, const GemvPlan& pl, hipStream_t str
 
 template <bool ROT>
 hipError_t launch_rows(GemvArgs a, int M, const GemvPlan& pl, hipStream_t stream) {
+  if (pl.rows_rs == 16) {
+    if (ROT) return hipErrorInvalidValue;  // the fused kernels use 32-row subtiles
+    switch (pl.rows_ns) {
+      case 1: return launch_rows_ns<1, 512, false, 16>(a, M, pl, stream);
+      case 2: return launch_rows_ns<2, 512, false, 16>(a, M, pl, stream);
+      case 3: return launch_rows_ns<3, 512, false, 16>(a, M, pl, stream);
+      case 4: return launch_rows_ns<4, 512, false, 16>(a, M, pl, stream);
+      case 5: return launch_rows_ns<5, 512, false, 16>(a, M, pl, stream);
+      case 6: return launch_rows_ns<6, 512, false, 16>(a, M, pl, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (pl.rows_ns) {
     case 1: return launch_rows_ns<1, 512, ROT>(a, M, pl, stream);
     case 2: return launch_rows_ns<2, 512, ROT>(a, M, pl, stream);
@@ -975,13 +1028,17 @@ hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* 
 
 // The fused decode kernel applies when the row-balanced plan does and the
 // whole rotation fits the workgroup: at most kRotMaxM tokens of at most
-// kRotMaxK, and at most kRotBlocksPerWave 1024-blocks per wave.
+// kRotMaxK, and at most 2 1024-blocks per wave (kRotBlocksPerWave = 3 for a
+// single token).
 bool gemv_rot_applies(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
   if (M < 1 || M > kRotMaxM || K > kRotMaxK || N < 1) return false;
   const GemvPlan pl = make_rows_plan(N, K, dev);
   if (pl.slices <= 0 || pl.rows_ns <= 0 || pl.gmax > 17 || pl.nw * 64 > 512 || pl.nw > (K >> 7))
     return false;
-  return M * (K >> 10) <= static_cast<int64_t>(kRotBlocksPerWave) * pl.nw;
+  // rotation rounds per wave: up to 2, or 3 for a single token (measured: 4
+  // tokens of K = 5120 in 3 rounds were no faster than the two launches)
+  const int64_t rounds = M == 1 ? kRotBlocksPerWave : 2;
+  return M * (K >> 10) <= rounds * pl.nw;
 }
 
 hipError_t launch_gemv_rot(const uint16_t* x, const int8_t* sign, bool silu, const uint8_t* packed,

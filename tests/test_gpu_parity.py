@@ -164,7 +164,10 @@ def test_gemm_ragged_shapes(twl, M, N, K):
                                  (10241, 2048), (24575, 1024), (24577, 1024),
                                  # one 32-row subtile: 16-17 rows per workgroup with
                                  # 3 groups per wave, 31-32 rows with 9 groups per wave
-                                 (4100, 3072), (8000, 9216)])
+                                 (4100, 3072), (8000, 9216),
+                                 # up to 16 tokens, 16-row subtiles: 16 rows per
+                                 # workgroup (one subtile), 62-63 rows (four)
+                                 (4096, 2048), (16000, 1024)])
 def test_gemv_vs_gemm_shapes(twl, M, N, K):
     # every decode kernel (automatic choice, dot4, MFMA) and the GEMM against
     # the oracle, bit-exact in acc
@@ -524,7 +527,8 @@ def test_plan_info_matches_workspace_and_family(twl, M, N, K, path, family):
 
 @pytest.mark.parametrize("M,N,K,silu,fused", [
     (1, 17408, 5120, False, True),   # decode gate/up: 5 blocks over 8 waves
-    (4, 17408, 5120, False, True),   # 20 blocks
+    (3, 24577, 2048, False, True),   # 6 blocks, two rounds of workgroups
+    (4, 17408, 5120, False, False),  # 20 blocks: 3 rounds for 4 tokens, two steps
     (3, 17408, 5120, True, True),    # the SiLU form
     (1, 5120, 17408, True, True),    # decode down with its SiLU input: 17 blocks
     (1, 5120, 17408, False, True),
