@@ -755,6 +755,7 @@ struct GemvPlan {
   int rows_ns = 0;   // subtiles of rows_rs rows per workgroup (0: not this kernel)
   int rows_rs = 32;
   int rows_wgs = 0;
+  int rows_p = 2;    // groups of loads in flight per wave when gmax == 5
 };
 
 // From this many tokens on, the matrix-core kernel beats the dot4 kernel
@@ -853,7 +854,19 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceI
       r.rows_rs = 16;
       r.rows_ns = static_cast<int>((rmax + 15) / 16);
     }
-    if (r.slices > 0) return r;
+    if (r.slices > 0) {
+      // Loads in flight for waves of 5 groups (K = 5120).  Two keep the
+      // workgroup at 65 KB of LDS, so that two share a CU where N needs two
+      // rounds of workgroups (5120 -> 34816).  With one round, more are
+      // faster where a workgroup has few subtiles: all five for at most two
+      // (5120 -> 5120, 20 rows: 5.63 -> 5.11 us at M = 1, 6.84 -> 6.55 at
+      // M = 24) and three for 16-row subtiles (5120 -> 17408, 68 rows: 8.51
+      // -> 8.31 us at M = 1, 9.91 -> 9.46 at M = 16); at M = 24 (three
+      // 32-row subtiles) three were slower (11.03 -> 11.29 us).
+      if (r.gmax == 5 && r.rows_wgs <= dev.cu_count)
+        r.rows_p = r.rows_ns <= 2 ? 5 : (r.rows_rs == 16 ? 3 : 2);
+      return r;
+    }
   }
   const bool want_mfma = kind == kGemvMfma || (kind == kGemvAuto && M >= kMfmaMinM);
   if (want_mfma && M <= 32) {
@@ -867,14 +880,27 @@ template <int NS, int MAXT, bool ROT = false, int RS = 32>
 hipError_t launch_rows_ns(GemvArgs a, int M, const GemvPlan& pl, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(pl.rows_wgs));
   const dim3 block(64 * pl.nw);
-  // groups of loads in flight per wave, within the register budget.  With 5
-  // groups per wave (K = 5120) two in flight leave the workgroup 65 KB of LDS
-  // and 123 VGPRs, so two workgroups share a CU (measured 4-18% faster than
-  // five in flight, most where N needs two rounds of workgroups).
+  // groups of loads in flight per wave, within the register budget: the
+  // plan's rows_p (2, 3 or 5) for 5-group waves, else 5 (3 for 3-group waves)
   constexpr int PM = 5;
   switch (pl.gmax) {
     case 3: hipLaunchKernelGGL((gemv_rows_kernel<NS, 3, 3, MAXT, ROT, RS>), grid, block, 0, stream, a, M); break;
-    case 5: hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 2, MAXT, ROT, RS>), grid, block, 0, stream, a, M); break;
+    case 5:
+      // the fused kernels keep two groups in flight (their x_i8 fills the LDS)
+      if constexpr (!ROT && NS <= 2) {
+        if (pl.rows_p == 5) {
+          hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 5, MAXT, false, RS>), grid, block, 0, stream, a, M);
+          break;
+        }
+      }
+      if constexpr (!ROT && RS == 16 && NS >= 3) {
+        if (pl.rows_p == 3) {
+          hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 3, MAXT, false, RS>), grid, block, 0, stream, a, M);
+          break;
+        }
+      }
+      hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 2, MAXT, ROT, RS>), grid, block, 0, stream, a, M);
+      break;
     case 9: hipLaunchKernelGGL((gemv_rows_kernel<NS, 9, PM, MAXT, ROT, RS>), grid, block, 0, stream, a, M); break;
     case 17: hipLaunchKernelGGL((gemv_rows_kernel<NS, 17, PM, MAXT, ROT, RS>), grid, block, 0, stream, a, M); break;
     case 33:
@@ -965,10 +991,11 @@ hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* 
   if (pl.slices > 1 && (part == nullptr || part_bytes < gemv_workspace_bytes(M, N, K, kind, dev)))
     return hipErrorInvalidValue;
   if (std::getenv("TWL_LOG"))
-    std::fprintf(stderr, "[twl] gemv%s M=%lld N=%lld K=%lld -> <= %d groups/wave, %d waves/WG, %d slices, grid=%d\n",
+    std::fprintf(stderr, "[twl] gemv%s M=%lld N=%lld K=%lld -> <= %d groups/wave, %d waves/WG, %d slices, grid=%d%s\n",
                  pl.rows_ns > 0 ? "-rows" : (pl.mfma ? "-mfma" : ""), static_cast<long long>(M),
                  static_cast<long long>(N), static_cast<long long>(K), pl.gmax, pl.nw, pl.slices,
-                 pl.rows_ns > 0 ? pl.rows_wgs : pl.n_rb * pl.slices);
+                 pl.rows_ns > 0 ? pl.rows_wgs : pl.n_rb * pl.slices,
+                 pl.rows_ns > 0 && pl.gmax == 5 ? (pl.rows_p == 5 ? ", 5 in flight" : pl.rows_p == 3 ? ", 3 in flight" : ", 2 in flight") : "");
   GemvArgs a = {};
   a.x = x_i8;
   a.a_scale = a_scale;

@@ -171,6 +171,20 @@ def test_gemm_ragged_shapes(twl, M, N, K):
 def test_gemv_vs_gemm_shapes(twl, M, N, K):
     # every decode kernel (automatic choice, dot4, MFMA) and the GEMM against
     # the oracle, bit-exact in acc
+    _gemv_vs_gemm(twl, M, N, K)
+
+
+@pytest.mark.parametrize("M", [1, 16, 24])
+@pytest.mark.parametrize("N,K", [
+    # 5-group waves (K = 5120) with more loads in flight: 20 and 16 rows per
+    # workgroup (all five groups), 68 rows in 16-row subtiles (three); two
+    # rounds of workgroups keep two in flight
+    (5120, 5120), (4096, 5120), (17407, 5120), (24577, 5120)])
+def test_gemv_prefetch_depths(twl, M, N, K):
+    _gemv_vs_gemm(twl, M, N, K)
+
+
+def _gemv_vs_gemm(twl, M, N, K):
     layer = W.make_layer(2000 + M * 7 + N, M, K, N)
     x_i8, a_scale = O.rotate_quant_act(layer.x_bits, layer.sign)
     packed, q, smax, oq, osm = _check_pack(twl, layer.code, layer.s_bits, "gemv")
