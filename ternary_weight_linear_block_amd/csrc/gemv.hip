@@ -422,8 +422,9 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(GemvArgs a, int M) {
 // Integer sums are exact, so A and B only have to agree on which k each
 // (lane group, byte) covers.  The waves split K into runs of at
 // most GMAX groups and keep P groups of loads in flight: group jj + P is issued
-// as soon as group jj has been consumed, so the stream and the unpack / MFMA
-// work overlap.  Loads are issued unconditionally (slots past the wave's run
+// as soon as group jj has been consumed (EARLY: as soon as group jj has landed,
+// into a (P + 1)-th buffer and activation slot, before group jj is computed),
+// so the stream and the unpack / MFMA work overlap.  Loads are issued unconditionally (slots past the wave's run
 // re-read its last group) so that the compiler's vmcnt waits stay static.
 // The activations of a group (at most kXRows tokens x 128 bytes) go to LDS
 // by direct loads with 8 lanes per 128-byte row, so each 1 KB load touches 16
@@ -461,7 +462,7 @@ struct RowGroup {
 // stays in LDS for the whole K and no activation is loaded per group.  The
 // rotation and the quantiser are those of rotate_quant_act (rotate_block.h),
 // so x_i8, a_scale and y equal the two-step result bit for bit.
-template <int NS, int GMAX, int P, int MAXT, bool ROT = false, int RS = 32>
+template <int NS, int GMAX, int P, int MAXT, bool ROT = false, int RS = 32, bool EARLY = false>
 __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
   static_assert(P >= 1 && P <= GMAX, "prefetch depth");
   static_assert(MAXT <= 64 * kRowsMaxWaves, "x slots are sized for 8 waves");
@@ -469,7 +470,10 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
   typedef typename std::conditional<RS == 32, v16i_t, v4i>::type acc_t;
   __shared__ int red[RS * NS * kRedStride];
   // per-wave group slots, or (ROT) all of x_i8: token t at t * (K + 16)
-  __shared__ __attribute__((aligned(1024))) int8_t xs[ROT ? kRotXBytes : kRowsMaxWaves * P * kXSlot];
+  // EARLY: group jj + P is issued as soon as group jj has landed, before
+  // group jj is computed, into a (P + 1)-th buffer and slot
+  constexpr int NB = EARLY ? P + 1 : P;
+  __shared__ __attribute__((aligned(1024))) int8_t xs[ROT ? kRotXBytes : kRowsMaxWaves * NB * kXSlot];
   __shared__ float rot_buf[ROT ? kRowsMaxWaves * rot::kWaveBufWords : 1];  // rotation transposes
   __shared__ unsigned tok_max[kRotMaxM];  // ROT: absmax bits of each token
   __shared__ float row_scale[32];        // a_scale of the tokens
@@ -571,14 +575,14 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
       xoff[i] = static_cast<uint32_t>(min(r, M - 1) * K + 16 * ((lane & 7) ^ chunk_swizzle(r)));
     }
     const void* xbase = sgpr_ptr(a.x);
-    const uint32_t xs_wave = lds_addr(xs) + static_cast<uint32_t>(wave * P * kXSlot);
+    const uint32_t xs_wave = lds_addr(xs) + static_cast<uint32_t>(wave * NB * kXSlot);
     // this lane's operand row in a slot (tokens past kXRows are never reduced)
     const int jr = min(j, kXRows - 1);
 
     // per group: NS weight loads (VGPR), then the xi activation DMAs; the
     // activation wait below counts on exactly this order.  The weights are
     // read once per call: nontemporal loads (measured 2-3% faster)
-    RowGroup<NS, RS> buf[P];
+    RowGroup<NS, RS> buf[NB];
     auto issue = [&](RowGroup<NS, RS>& d, int jj) {
       const int g = g0 + min(jj, ng - 1);
 #pragma unroll
@@ -594,7 +598,7 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
         }
       }
       if (!ROT) {
-        const uint32_t slot = __builtin_amdgcn_readfirstlane(xs_wave + (jj % P) * kXSlot);
+        const uint32_t slot = __builtin_amdgcn_readfirstlane(xs_wave + (jj % NB) * kXSlot);
         const uint32_t gx = static_cast<uint32_t>(g) * 128;
         dma16xn(xi, xbase, xoff[0] + gx, xoff[1] + gx, xoff[2] + gx, slot, slot + 1024, slot + 2048);
       }
@@ -654,12 +658,13 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
     for (int s = 0; s < NS; ++s) acc[s] = acc_t{0};
 #pragma unroll
     for (int jj = 0; jj < GMAX; ++jj) {
-      RowGroup<NS, RS>& d = buf[jj % P];
+      RowGroup<NS, RS>& d = buf[jj % NB];
       // this group's activation DMAs are done once at most the loads of the
       // groups issued after it are outstanding (NS + xi per group; counting
       // NS + 1 only makes the wait stricter)
       if (!ROT) wait_groups_after<NS + 1>(min(P - 1, GMAX - 1 - jj));
       asm volatile("" ::: "memory");
+      if (EARLY && jj + P < GMAX) issue(buf[(jj + P) % NB], jj + P);
       if (jj == 0 || jj < ng) {
         // k-chunks (16 bytes) of the group this lane supplies: RS = 32, chunk
         // 4 h + t for MFMA t = 0..3; RS = 16, chunk 2 h + t for MFMA t = 0, 1
@@ -670,7 +675,7 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
 #pragma unroll
           for (int t = 0; t < NT; ++t) xv[t] = *reinterpret_cast<const v4i*>(xr + 16 * t);
         } else {
-          const int8_t* xr = xs + (wave * P + jj % P) * kXSlot + jr * 128;
+          const int8_t* xr = xs + (wave * NB + jj % NB) * kXSlot + jr * 128;
 #pragma unroll
           for (int t = 0; t < NT; ++t)
             xv[t] = *reinterpret_cast<const v4i*>(xr + 16 * ((NT * h + t) ^ chunk_swizzle(jr)));
@@ -691,7 +696,7 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
           }
         }
       }
-      if (jj + P < GMAX) issue(d, jj + P);
+      if (!EARLY && jj + P < GMAX) issue(d, jj + P);
     }
     // exact cross-wave reduction; lane (j, h) holds token j and, in register
     // r, row 8 (r / 4) + 4 h + (r % 4) of each subtile
@@ -755,7 +760,8 @@ struct GemvPlan {
   int rows_ns = 0;   // subtiles of rows_rs rows per workgroup (0: not this kernel)
   int rows_rs = 32;
   int rows_wgs = 0;
-  int rows_p = 2;    // groups of loads in flight per wave when gmax == 5
+  int rows_p = 2;    // groups of loads in flight per wave when gmax is 5 or 17
+  bool rows_early = false;  // issue a group's successor before computing it
 };
 
 // From this many tokens on, the matrix-core kernel beats the dot4 kernel
@@ -855,16 +861,34 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceI
       r.rows_ns = static_cast<int>((rmax + 15) / 16);
     }
     if (r.slices > 0) {
-      // Loads in flight for waves of 5 groups (K = 5120).  Two keep the
-      // workgroup at 65 KB of LDS, so that two share a CU where N needs two
-      // rounds of workgroups (5120 -> 34816).  With one round, more are
-      // faster where a workgroup has few subtiles: all five for at most two
-      // (5120 -> 5120, 20 rows: 5.63 -> 5.11 us at M = 1, 6.84 -> 6.55 at
-      // M = 24) and three for 16-row subtiles (5120 -> 17408, 68 rows: 8.51
-      // -> 8.31 us at M = 1, 9.91 -> 9.46 at M = 16); at M = 24 (three
-      // 32-row subtiles) three were slower (11.03 -> 11.29 us).
-      if (r.gmax == 5 && r.rows_wgs <= dev.cu_count)
-        r.rows_p = r.rows_ns <= 2 ? 5 : (r.rows_rs == 16 ? 3 : 2);
+      // Loads in flight per wave, measured (µs, alternating on one box):
+      // - 5-group waves (K = 5120) keep two by default (the workgroup then
+      //   needs 65 KB of LDS, so two share a CU where N needs two rounds of
+      //   workgroups, 5120 -> 34816).
+      // - With 32-row subtiles (17..24 tokens) one group in flight, the next
+      //   issued as soon as it has landed, before it is computed ("early"),
+      //   is faster: 10.59 -> 9.66 on 5120 -> 17408, 16.94 -> 15.96 on
+      //   5120 -> 34816, 6.57 -> 6.45 on 5120 -> 5120 at M = 24.
+      // - With one round of workgroups and 16-row subtiles: all five at most
+      //   two subtiles (5120 -> 5120, 20 rows: 5.63 -> 5.11 at M = 1), three
+      //   early with more (5120 -> 17408: 8.51 -> 8.30 at M = 1, 9.91 ->
+      //   9.24 at M = 16).
+      // - 17-group waves (K = 17408) keep five; with 16-row subtiles three
+      //   early are faster (5120 <- 17408: 9.71 -> 9.49 at M = 1, 9.79 ->
+      //   9.60 at M = 8), with 32-row subtiles slower (13.36 -> 15.08).
+      const bool one_round = r.rows_wgs <= dev.cu_count;
+      if (r.gmax == 5) {
+        if (r.rows_rs == 32) {
+          r.rows_p = 1;
+          r.rows_early = true;
+        } else if (one_round) {
+          r.rows_p = r.rows_ns <= 2 ? 5 : 3;
+          r.rows_early = r.rows_ns > 2;
+        }
+      } else if (r.gmax == 17 && r.rows_rs == 16 && one_round) {
+        r.rows_p = 3;
+        r.rows_early = true;
+      }
       return r;
     }
   }
@@ -881,28 +905,48 @@ hipError_t launch_rows_ns(GemvArgs a, int M, const GemvPlan& pl, hipStream_t str
   const dim3 grid(static_cast<unsigned>(pl.rows_wgs));
   const dim3 block(64 * pl.nw);
   // groups of loads in flight per wave, within the register budget: the
-  // plan's rows_p (2, 3 or 5) for 5-group waves, else 5 (3 for 3-group waves)
+  // plan's rows_p and rows_early for 5- and 17-group waves, else 5 (3 for
+  // 3-group waves)
   constexpr int PM = 5;
   switch (pl.gmax) {
     case 3: hipLaunchKernelGGL((gemv_rows_kernel<NS, 3, 3, MAXT, ROT, RS>), grid, block, 0, stream, a, M); break;
     case 5:
+      if constexpr (!ROT) {
+        if (pl.rows_early) {
+          if constexpr (RS == 32) {
+            if (pl.rows_p == 1) {
+              hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 1, MAXT, false, RS, true>), grid, block, 0, stream, a, M);
+              break;
+            }
+          }
+          if constexpr (RS == 16 && NS >= 3) {
+            if (pl.rows_p == 3) {
+              hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 3, MAXT, false, RS, true>), grid, block, 0, stream, a, M);
+              break;
+            }
+          }
+          return hipErrorInvalidValue;
+        }
+        if constexpr (RS == 16 && NS <= 2) {
+          if (pl.rows_p == 5) {
+            hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 5, MAXT, false, RS>), grid, block, 0, stream, a, M);
+            break;
+          }
+        }
+      }
       // the fused kernels keep two groups in flight (their x_i8 fills the LDS)
-      if constexpr (!ROT && NS <= 2) {
-        if (pl.rows_p == 5) {
-          hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 5, MAXT, false, RS>), grid, block, 0, stream, a, M);
-          break;
-        }
-      }
-      if constexpr (!ROT && RS == 16 && NS >= 3) {
-        if (pl.rows_p == 3) {
-          hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 3, MAXT, false, RS>), grid, block, 0, stream, a, M);
-          break;
-        }
-      }
       hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 2, MAXT, ROT, RS>), grid, block, 0, stream, a, M);
       break;
     case 9: hipLaunchKernelGGL((gemv_rows_kernel<NS, 9, PM, MAXT, ROT, RS>), grid, block, 0, stream, a, M); break;
-    case 17: hipLaunchKernelGGL((gemv_rows_kernel<NS, 17, PM, MAXT, ROT, RS>), grid, block, 0, stream, a, M); break;
+    case 17:
+      if constexpr (!ROT && RS == 16) {
+        if (pl.rows_early && pl.rows_p == 3) {
+          hipLaunchKernelGGL((gemv_rows_kernel<NS, 17, 3, MAXT, false, RS, true>), grid, block, 0, stream, a, M);
+          break;
+        }
+      }
+      hipLaunchKernelGGL((gemv_rows_kernel<NS, 17, PM, MAXT, ROT, RS>), grid, block, 0, stream, a, M);
+      break;
     case 33:
       // K > kRotMaxK: never planned with ROT
       if (ROT) return hipErrorInvalidValue;
@@ -995,7 +1039,8 @@ hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* 
                  pl.rows_ns > 0 ? "-rows" : (pl.mfma ? "-mfma" : ""), static_cast<long long>(M),
                  static_cast<long long>(N), static_cast<long long>(K), pl.gmax, pl.nw, pl.slices,
                  pl.rows_ns > 0 ? pl.rows_wgs : pl.n_rb * pl.slices,
-                 pl.rows_ns > 0 && pl.gmax == 5 ? (pl.rows_p == 5 ? ", 5 in flight" : pl.rows_p == 3 ? ", 3 in flight" : ", 2 in flight") : "");
+                 pl.rows_ns > 0 && pl.rows_early ? (pl.rows_p == 1 ? ", 1 in flight, early" : ", 3 in flight, early")
+                 : pl.rows_ns > 0 && pl.gmax == 5 ? (pl.rows_p == 5 ? ", 5 in flight" : ", 2 in flight") : "");
   GemvArgs a = {};
   a.x = x_i8;
   a.a_scale = a_scale;

@@ -57,7 +57,10 @@ def test_m0_only_feeds_our_lds_loads(tmp_path_factory, asm, src):
     kernels = _kernels(text, kernel, least)
     for name, body in kernels.items():
         lines = [ln.strip() for ln in body.splitlines() if ln.strip() and not ln.strip().startswith(";")]
-        if src == "gemv.hip" and "ELb1E" in name:  # ROT = true
+        # gemv_rows_kernel<NS, GMAX, P, MAXT, ROT, RS, EARLY>: ROT is the fifth
+        # template argument (the first bool)
+        rot = re.search(r"gemv_rows_kernelI(?:Li\d+E){4}Lb([01])E", name)
+        if src == "gemv.hip" and rot and rot.group(1) == "1":
             # the fused-rotation decode kernels quantise x into LDS themselves:
             # no direct loads, and so no M0 at all
             assert not any("global_load_lds" in ln or "m0" in ln for ln in lines), name

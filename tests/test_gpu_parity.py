@@ -176,10 +176,12 @@ def test_gemv_vs_gemm_shapes(twl, M, N, K):
 
 @pytest.mark.parametrize("M", [1, 16, 24])
 @pytest.mark.parametrize("N,K", [
-    # 5-group waves (K = 5120) with more loads in flight: 20 and 16 rows per
-    # workgroup (all five groups), 68 rows in 16-row subtiles (three); two
-    # rounds of workgroups keep two in flight
-    (5120, 5120), (4096, 5120), (17407, 5120), (24577, 5120)])
+    # 5-group waves (K = 5120), each depth of loads in flight the planner
+    # picks: 20 and 16 rows per workgroup (all five at M <= 16), 67-68 rows
+    # in 16-row subtiles (three, issued early), two rounds of workgroups (two);
+    # 32-row subtiles at M = 24 (one, issued early) on every shape;
+    # 17-group waves (K = 17408) with 16-row subtiles (three, early)
+    (5120, 5120), (4096, 5120), (17407, 5120), (24577, 5120), (6000, 17408)])
 def test_gemv_prefetch_depths(twl, M, N, K):
     _gemv_vs_gemm(twl, M, N, K)
 
