@@ -432,6 +432,13 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(GemvArgs a, int M) {
 // would touch 64 per instruction, and the address unit, not HBM, would bound
 // the kernel.  Each wave owns P slots, one per group in flight.
 constexpr int kXRows = 24;              // the decode paths take M <= 24
+// Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format
+// (DATA_FORMAT = 4 in bits 15..18), no swizzle, no index stride, so the
+// range check is a plain byte count.
+constexpr int kRawBufferWord3 = 0x00020000;
+// cache-policy operand of the buffer loads: nontemporal (the weights are read
+// once per call)
+constexpr int kCacheNonTemporal = 2;
 constexpr int kXSlot = kXRows * 128;    // bytes per group slot
 constexpr int kRowsMaxWaves = 8;
 // Fused rotation (ROT): at most kRotMaxM tokens of at most kRotMaxK, each wave
@@ -510,11 +517,21 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
     const int j = lane & (RS - 1), h = lane / RS;
     // lanes past the last row of this workgroup re-read that row: the same
     // cache lines, so no bytes beyond the workgroup's own rows are fetched
-    size_t wbase[NS];
+    // weights through a buffer resource: its base is the workgroup's first
+    // row block and its range the row blocks the workgroup's rows touch (at
+    // most three of G x 2 KB; a load outside it would return zeros instead of
+    // reading another workgroup's rows).  A load then takes its lane offset
+    // from a VGPR and the group's offset from an SGPR: no address arithmetic
+    // per load.
+    const int rb0 = r0 >> 6;
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.packed) + static_cast<size_t>(rb0) * G * 2048, 0,
+        (((r1 - 1) >> 6) - rb0 + 1) * G * 2048, kRawBufferWord3);
+    uint32_t wbase[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int n = min(r0 + RS * s + j, r1 - 1);
-      wbase[s] = static_cast<size_t>(n >> 6) * G * 2048 + (n & 63) * 32 + h * (RS == 32 ? 16 : 8);
+      wbase[s] = static_cast<uint32_t>(((n >> 6) - (r0 >> 6)) * G * 2048 + (n & 63) * 32 + h * (RS == 32 ? 16 : 8));
     }
     // ROT: this wave's blocks of x (block bi = wave + i nw of the M x K/1024
     // blocks is token bi / nblk, block bi % nblk), loaded first: waits complete
@@ -588,12 +605,10 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         if constexpr (RS == 32) {
-          const u32x4 t = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4*>(a.packed + wbase[s] + static_cast<size_t>(g) * 2048));
+          const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(wres, wbase[s], g * 2048, kCacheNonTemporal);
           d.w[s] = make_uint4(t.x, t.y, t.z, t.w);
         } else {
-          const u32x2 t = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x2*>(a.packed + wbase[s] + static_cast<size_t>(g) * 2048));
+          const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(wres, wbase[s], g * 2048, kCacheNonTemporal);
           d.w[s] = make_uint2(t.x, t.y);
         }
       }
