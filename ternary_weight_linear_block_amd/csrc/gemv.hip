@@ -485,6 +485,15 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
   __shared__ unsigned tok_max[kRotMaxM];  // ROT: absmax bits of each token
   __shared__ float row_scale[32];        // a_scale of the tokens
   __shared__ float col_scale[RS * NS];   // smax of the rows
+  // QLDS: the workgroup's rows of q (R x G bytes, contiguous in q, G <= 8
+  // GMAX) staged in LDS by coalesced loads, instead of per-lane gathers of
+  // the lane's rows (measured, µs: 5120 <- 17408 9.58 -> 8.78 at M = 1 and
+  // 13.61 -> 13.18 at M = 24, 5120 -> 17408 8.49 -> 8.25 at M = 1; with
+  // 32-row subtiles on 5-group waves, one group in flight, the barrier that
+  // publishes the staged rows cost more than it saved: 11.83 -> 12.12 at M =
+  // 24 on 5120 -> 17408, so those keep the gathers)
+  constexpr bool QLDS = !ROT && GMAX <= 17 && !(GMAX == 5 && RS == 32);
+  __shared__ __attribute__((aligned(16))) int8_t qs[QLDS ? RS * NS * GMAX * 8 : 4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
@@ -564,22 +573,40 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
     typedef uint32_t qvec __attribute__((ext_vector_type(QV)));
     const int qa = g0 & ~3, qsh = g0 & 3;
     const int qd_last = (G - qa) / 4 - 1;
-    qvec qw[NS];  // indexed by constants only (unrolled), so kept in registers
+    qvec qw[QLDS ? 1 : NS];  // indexed by constants only (unrolled), so kept in registers
+    // QLDS: dwords t, t + blockDim, ... of the workgroup's R x G bytes of q
+    // (from q[r0, 0]: G % 8 == 0, so dword aligned), clamped so that every
+    // slot loads (no branch around loads in flight) and written to LDS once
+    // the first groups of weights are issued
+    constexpr int QI = QLDS ? (RS * NS * GMAX * 2 + MAXT - 1) / MAXT : 1;
+    const int qdw = R * G / 4;
+    uint32_t qr[QI];
+    if constexpr (QLDS) {
+      const uint32_t* qsrc = reinterpret_cast<const uint32_t*>(a.q + static_cast<size_t>(r0) * G);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int n = min(r0 + RS * s + j, r1 - 1);
-      const uint32_t* qrow = reinterpret_cast<const uint32_t*>(a.q + static_cast<size_t>(n) * G + qa);
-      qvec v = {};
+      for (int i = 0; i < QI; ++i) qr[i] = qsrc[min(static_cast<int>(threadIdx.x) + i * MAXT, qdw - 1)];
+    } else {
 #pragma unroll
-      for (int d = 0; d < QD; ++d) v[d] = qrow[min(d, qd_last)];
-      qw[s] = v;
+      for (int s = 0; s < NS; ++s) {
+        const int n = min(r0 + RS * s + j, r1 - 1);
+        const uint32_t* qrow = reinterpret_cast<const uint32_t*>(a.q + static_cast<size_t>(n) * G + qa);
+        qvec v = {};
+#pragma unroll
+        for (int d = 0; d < QD; ++d) v[d] = qrow[min(d, qd_last)];
+        qw[s] = v;
+      }
     }
-    // q[n, g0 + jj]: byte qsh + jj of the run (jj is a constant once unrolled):
-    // a 64-bit shift of two dwords picked by constant indices
+    // q[n, g0 + jj]: QLDS, one byte of the staged rows; else byte qsh + jj of
+    // the lane's run (jj is a constant once unrolled): a 64-bit shift of two
+    // dwords picked by constant indices
     const auto qbyte = [&](int s, int jj) {
-      const qvec& v = qw[s];
-      const uint64_t w = (static_cast<uint64_t>(v[(jj >> 2) + 1]) << 32) | v[jj >> 2];
-      return static_cast<int>(static_cast<int8_t>(w >> (8 * (qsh + (jj & 3)))));
+      if constexpr (QLDS) {
+        return static_cast<int>(qs[min(RS * s + j, R - 1) * G + g0 + min(jj, ng - 1)]);
+      } else {
+        const qvec& v = qw[s];
+        const uint64_t w = (static_cast<uint64_t>(v[(jj >> 2) + 1]) << 32) | v[jj >> 2];
+        return static_cast<int>(static_cast<int8_t>(w >> (8 * (qsh + (jj & 3)))));
+      }
     };
     // activation DMA: instruction i, lane l -> LDS row r = 8 i + l / 8 (token
     // min(r, M - 1)), LDS chunk l % 8 holding global chunk (l % 8) ^ swizzle(r);
@@ -589,7 +616,11 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       const int r = 8 * i + (lane >> 3);
-      xoff[i] = static_cast<uint32_t>(min(r, M - 1) * K + 16 * ((lane & 7) ^ chunk_swizzle(r)));
+      // 24-bit multiply (tokens < 24, K <= 2^16): a 32-bit result, so the
+      // compiler does not form a 64-bit multiply-add whose unused high half
+      // could be a register still waiting on a load
+      xoff[i] = __umul24(static_cast<uint32_t>(min(r, M - 1)), static_cast<uint32_t>(K)) +
+                static_cast<uint32_t>(16 * ((lane & 7) ^ chunk_swizzle(r)));
     }
     const void* xbase = sgpr_ptr(a.x);
     const uint32_t xs_wave = lds_addr(xs) + static_cast<uint32_t>(wave * NB * kXSlot);
@@ -680,6 +711,17 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
       if (!ROT) wait_groups_after<NS + 1>(min(P - 1, GMAX - 1 - jj));
       asm volatile("" ::: "memory");
       if (EARLY && jj + P < GMAX) issue(buf[(jj + P) % NB], jj + P);
+      if (QLDS && jj == 0) {
+        // the q loads were issued before the weights, so they have landed;
+        // every wave has groups (the planner keeps nw <= G), so all reach
+        // the barrier
+#pragma unroll
+        for (int i = 0; i < QI; ++i) {
+          const int d = static_cast<int>(threadIdx.x) + i * MAXT;
+          if (d < qdw) reinterpret_cast<uint32_t*>(qs)[d] = qr[i];
+        }
+        __syncthreads();
+      }
       if (jj == 0 || jj < ng) {
         // k-chunks (16 bytes) of the group this lane supplies: RS = 32, chunk
         // 4 h + t for MFMA t = 0..3; RS = 16, chunk 2 h + t for MFMA t = 0, 1
@@ -919,6 +961,8 @@ template <int NS, int MAXT, bool ROT = false, int RS = 32>
 hipError_t launch_rows_ns(GemvArgs a, int M, const GemvPlan& pl, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(pl.rows_wgs));
   const dim3 block(64 * pl.nw);
+  // the kernel stages q with MAXT threads (nw = 8 whenever K >= 1024)
+  if (64 * pl.nw != MAXT) return hipErrorInvalidValue;
   // groups of loads in flight per wave, within the register budget: the
   // plan's rows_p and rows_early for 5- and 17-group waves, else 5 (3 for
   // 3-group waves)
