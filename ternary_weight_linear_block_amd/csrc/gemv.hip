@@ -491,8 +491,9 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
   // 13.61 -> 13.18 at M = 24, 5120 -> 17408 8.49 -> 8.25 at M = 1; with
   // 32-row subtiles on 5-group waves, one group in flight, the barrier that
   // publishes the staged rows cost more than it saved: 11.83 -> 12.12 at M =
-  // 24 on 5120 -> 17408, so those keep the gathers)
-  constexpr bool QLDS = !ROT && GMAX <= 17 && !(GMAX == 5 && RS == 32);
+  // 24 on 5120 -> 17408, so those keep the gathers; the fused kernels
+  // publish the rows with the barriers their rotation already has)
+  constexpr bool QLDS = GMAX <= 17 && (ROT || !(GMAX == 5 && RS == 32));
   __shared__ __attribute__((aligned(16))) int8_t qs[QLDS ? RS * NS * GMAX * 8 : 4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -675,6 +676,14 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
           if (lane == 0) atomicMax(&tok_max[t], __float_as_uint(m));
         }
       }
+      if constexpr (QLDS) {
+        // the staged q rows, published by the barriers of the rotation
+#pragma unroll
+        for (int i = 0; i < QI; ++i) {
+          const int d = static_cast<int>(threadIdx.x) + i * MAXT;
+          if (d < qdw) reinterpret_cast<uint32_t*>(qs)[d] = qr[i];
+        }
+      }
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < kRotBlocksPerWave; ++i) {
@@ -711,7 +720,7 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
       if (!ROT) wait_groups_after<NS + 1>(min(P - 1, GMAX - 1 - jj));
       asm volatile("" ::: "memory");
       if (EARLY && jj + P < GMAX) issue(buf[(jj + P) % NB], jj + P);
-      if (QLDS && jj == 0) {
+      if (QLDS && !ROT && jj == 0) {
         // the q loads were issued before the weights, so they have landed;
         // every wave has groups (the planner keeps nw <= G), so all reach
         // the barrier
