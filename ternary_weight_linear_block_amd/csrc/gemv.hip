@@ -1028,22 +1028,25 @@ hipError_t launch_rows_ns(GemvArgs a, int M, const GemvPlan& pl, hipStream_t str
 template <bool ROT>
 hipError_t launch_rows(GemvArgs a, int M, const GemvPlan& pl, hipStream_t stream) {
   if (pl.rows_rs == 16) {
-    if (ROT) return hipErrorInvalidValue;  // the fused kernels use 32-row subtiles
     switch (pl.rows_ns) {
-      case 1: return launch_rows_ns<1, 512, false, 16>(a, M, pl, stream);
-      case 2: return launch_rows_ns<2, 512, false, 16>(a, M, pl, stream);
-      case 3: return launch_rows_ns<3, 512, false, 16>(a, M, pl, stream);
-      case 4: return launch_rows_ns<4, 512, false, 16>(a, M, pl, stream);
-      case 5: return launch_rows_ns<5, 512, false, 16>(a, M, pl, stream);
-      case 6: return launch_rows_ns<6, 512, false, 16>(a, M, pl, stream);
+      case 1: return launch_rows_ns<1, 512, ROT, 16>(a, M, pl, stream);
+      case 2: return launch_rows_ns<2, 512, ROT, 16>(a, M, pl, stream);
+      case 3: return launch_rows_ns<3, 512, ROT, 16>(a, M, pl, stream);
+      case 4: return launch_rows_ns<4, 512, ROT, 16>(a, M, pl, stream);
+      case 5: return launch_rows_ns<5, 512, ROT, 16>(a, M, pl, stream);
+      case 6: return launch_rows_ns<6, 512, ROT, 16>(a, M, pl, stream);
       default: return hipErrorInvalidValue;
     }
   }
-  switch (pl.rows_ns) {
-    case 1: return launch_rows_ns<1, 512, ROT>(a, M, pl, stream);
-    case 2: return launch_rows_ns<2, 512, ROT>(a, M, pl, stream);
-    case 3: return launch_rows_ns<3, 512, ROT>(a, M, pl, stream);
-    default: return hipErrorInvalidValue;
+  if constexpr (ROT) {
+    return hipErrorInvalidValue;  // the fused kernels use 16-row subtiles
+  } else {
+    switch (pl.rows_ns) {
+      case 1: return launch_rows_ns<1, 512, false>(a, M, pl, stream);
+      case 2: return launch_rows_ns<2, 512, false>(a, M, pl, stream);
+      case 3: return launch_rows_ns<3, 512, false>(a, M, pl, stream);
+      default: return hipErrorInvalidValue;
+    }
   }
 }
 
@@ -1186,7 +1189,11 @@ hipError_t launch_gemv_rot(const uint16_t* x, const int8_t* sign, bool silu, con
                            void* out, OutKind out_kind, int8_t* x_i8, float* a_scale,
                            const DeviceInfo& dev, hipStream_t stream) {
   if (!gemv_rot_applies(M, N, K, dev)) return hipErrorNotSupported;
-  const GemvPlan pl = make_rows_plan(N, K, dev);
+  // 16-row subtiles and v_mfma_i32_16x16x64_i8, tokens padded to 16, as the
+  // two-step path uses at these batch sizes
+  GemvPlan pl = make_rows_plan(N, K, dev);
+  pl.rows_rs = 16;
+  pl.rows_ns = static_cast<int>((N + pl.rows_wgs - 1) / pl.rows_wgs + 15) / 16;
   if (std::getenv("TWL_LOG"))
     std::fprintf(stderr, "[twl] gemv-rows+rotation M=%lld N=%lld K=%lld silu=%d -> <= %d groups/wave, %d waves/WG, grid=%d\n",
                  static_cast<long long>(M), static_cast<long long>(N), static_cast<long long>(K),
