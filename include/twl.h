@@ -274,9 +274,10 @@ twl_status twl_plan_info(int64_t M, int64_t N, int64_t K, int path, int64_t* inf
  *   x_i8      out: int8 [M, K];  a_scale out: fp32 [M]  (device, caller-owned)
  *   out       out: [M, N] of the out_kind (twl_out)
  *   workspace     : as ternary_linear_ex for this M, N, K (twl_workspace_bytes)
- * For small decode batches (at most 4 tokens, K <= 17408, at most 2 1024-blocks
+ * For small decode batches (at most 2 tokens, K <= 17408, at most 2 1024-blocks
  * of rotation per wave of a decode workgroup, 3 for a single token, on shapes
- * where the row-balanced decode kernel applies) one fused kernel does both steps: every decode
+ * where the row-balanced decode kernel covers N with one workgroup per CU)
+ * one fused kernel does both steps: every decode
  * workgroup rotates and quantises the tokens itself while its first weight
  * loads are in flight, which removes the rotation's own launch from the
  * decode step.  Other shapes run the two kernels back to back on `stream`.

@@ -445,7 +445,7 @@ constexpr int kRowsMaxWaves = 8;
 // rotating at most kRotBlocksPerWave 1024-blocks; all of x_i8 then stays in
 // LDS, rows padded by 16 bytes (so that the tokens' 16-byte reads fall on
 // different banks).
-constexpr int kRotMaxM = 4;
+constexpr int kRotMaxM = 2;
 constexpr int kRotMaxK = 17408;
 constexpr int kRotBlocksPerWave = 3;
 constexpr int kRotXBytes = kRotMaxM * (kRotMaxK + 16);
@@ -1169,17 +1169,21 @@ hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* 
 }
 
 
-// The fused decode kernel applies when the row-balanced plan does and the
-// whole rotation fits the workgroup: at most kRotMaxM tokens of at most
-// kRotMaxK, and at most 2 1024-blocks per wave (kRotBlocksPerWave = 3 for a
-// single token).
+// The fused decode kernel applies when the row-balanced plan does with one
+// round of workgroups and the whole rotation fits the workgroup: at most
+// kRotMaxM tokens of at most kRotMaxK, and at most 2 1024-blocks per wave
+// (kRotBlocksPerWave = 3 for a single token).  Measured against the two
+// launches (µs): 5120 -> 17408 9.7 / 12.0 at M = 1, 10.5 / 11.6 at M = 2,
+// but 11.8 / 11.5 at M = 3 and 12.3 / 12.0 at M = 4 (three rounds of
+// rotation per wave); 5120 -> 5120 7.4 / 8.5 at M = 1, 9.3 / 8.4 at M = 3;
+// 5120 -> 34816 (two rounds of workgroups, each rotating again) 18.0 / 14.5
+// at M = 1.
 bool gemv_rot_applies(int64_t M, int64_t N, int64_t K, const DeviceInfo& dev) {
   if (M < 1 || M > kRotMaxM || K > kRotMaxK || N < 1) return false;
   const GemvPlan pl = make_rows_plan(N, K, dev);
   if (pl.slices <= 0 || pl.rows_ns <= 0 || pl.gmax > 17 || pl.nw * 64 > 512 || pl.nw > (K >> 7))
     return false;
-  // rotation rounds per wave: up to 2, or 3 for a single token (measured: 4
-  // tokens of K = 5120 in 3 rounds were no faster than the two launches)
+  if (pl.rows_wgs > dev.cu_count) return false;
   const int64_t rounds = M == 1 ? kRotBlocksPerWave : 2;
   return M * (K >> 10) <= rounds * pl.nw;
 }

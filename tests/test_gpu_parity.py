@@ -546,15 +546,17 @@ def test_plan_info_matches_workspace_and_family(twl, M, N, K, path, family):
 
 @pytest.mark.parametrize("M,N,K,silu,fused", [
     (1, 17408, 5120, False, True),   # decode gate/up: 5 blocks over 8 waves
-    (3, 24577, 2048, False, True),   # 6 blocks, two rounds of workgroups
-    (4, 17408, 5120, False, False),  # 20 blocks: 3 rounds for 4 tokens, two steps
-    (3, 17408, 5120, True, True),    # the SiLU form
+    (2, 17408, 5120, True, True),    # the SiLU form, 10 blocks
+    (2, 16001, 2048, False, True),   # ragged rows (62-63 per workgroup), 4 blocks
     (1, 5120, 17408, True, True),    # decode down with its SiLU input: 17 blocks
     (1, 5120, 17408, False, True),
-    (2, 24577, 1024, False, True),   # two rounds of workgroups, ragged rows
-    (1, 8000, 9216, True, True),     # one 32-row subtile, 9 groups per wave
-    (2, 5120, 17408, False, False),  # 34 blocks: more than 3 per wave, two steps
-    (5, 17408, 5120, False, False),  # more than 4 tokens
+    (1, 8000, 9216, True, True),     # 31-32 rows per workgroup, 9 groups per wave
+    (3, 24577, 2048, False, False),  # three tokens: two steps
+    (4, 17408, 5120, False, False),
+    (2, 24577, 1024, False, False),  # two rounds of workgroups: two steps
+    (1, 34816, 5120, False, False),
+    (2, 5120, 17408, False, False),  # 34 blocks: more than 2 per wave, two steps
+    (5, 17408, 5120, False, False),
     (64, 2048, 2048, True, False),   # prefill: the GEMM path
 ])
 def test_rotate_quant_linear(twl, M, N, K, silu, fused):
@@ -564,7 +566,7 @@ def test_rotate_quant_linear(twl, M, N, K, silu, fused):
         ox, osc = O.silu_mul_rotate_quant_act(xin, sign)
     else:
         xin, sign = layer.x_bits.copy(), layer.sign
-        if M >= 3:
+        if M >= 2:
             xin[1] = 0  # an all-zero token: a_scale 0, x_i8 0
         ox, osc = O.rotate_quant_act(xin, sign)
     packed, q, smax = gpu_pack(twl, layer.code, layer.s_bits)
