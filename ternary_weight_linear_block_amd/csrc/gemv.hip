@@ -422,15 +422,17 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(GemvArgs a, int M) {
 // Integer sums are exact, so A and B only have to agree on which k each
 // (lane group, byte) covers.  The waves split K into runs of at
 // most GMAX groups and keep P groups of loads in flight: group jj + P is issued
-// as soon as group jj has been consumed (EARLY: as soon as group jj has landed,
-// into a (P + 1)-th buffer and activation slot, before group jj is computed),
-// so the stream and the unpack / MFMA work overlap.  Loads are issued unconditionally (slots past the wave's run
-// re-read its last group) so that the compiler's vmcnt waits stay static.
+// as soon as group jj has been consumed (EARLY: as soon as group jj has
+// landed, into a (P + 1)-th buffer and activation slot, before group jj is
+// computed), so the stream and the unpack / MFMA work overlap.  Loads are
+// issued unconditionally (slots past the wave's run re-read its last group)
+// so that the compiler's vmcnt waits stay static.
 // The activations of a group (at most kXRows tokens x 128 bytes) go to LDS
 // by direct loads with 8 lanes per 128-byte row, so each 1 KB load touches 16
 // cache lines; read as MFMA operands (16 bytes of one token per lane) they
 // would touch 64 per instruction, and the address unit, not HBM, would bound
-// the kernel.  Each wave owns P slots, one per group in flight.
+// the kernel.  Each wave owns P slots (P + 1 with EARLY), one per group in
+// flight.
 constexpr int kXRows = 24;              // the decode paths take M <= 24
 // Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format
 // (DATA_FORMAT = 4 in bits 15..18), no swizzle, no index stride, so the
@@ -575,10 +577,11 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
     const int qa = g0 & ~3, qsh = g0 & 3;
     const int qd_last = (G - qa) / 4 - 1;
     qvec qw[QLDS ? 1 : NS];  // indexed by constants only (unrolled), so kept in registers
-    // QLDS: dwords t, t + blockDim, ... of the workgroup's R x G bytes of q
-    // (from q[r0, 0]: G % 8 == 0, so dword aligned), clamped so that every
-    // slot loads (no branch around loads in flight) and written to LDS once
-    // the first groups of weights are issued
+    // QLDS: dwords t, t + MAXT, ... of the workgroup's R x G bytes of q (from
+    // q[r0, 0]: G % 8 == 0, so dword aligned), clamped so that every slot
+    // loads (no branch around loads in flight), issued ahead of the weights
+    // and written to LDS once the first group has landed (fused: before the
+    // rotation's first barrier)
     constexpr int QI = QLDS ? (RS * NS * GMAX * 2 + MAXT - 1) / MAXT : 1;
     const int qdw = R * G / 4;
     uint32_t qr[QI];
