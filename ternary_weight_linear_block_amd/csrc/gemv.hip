@@ -471,9 +471,15 @@ struct RowGroup {
 // stays in LDS for the whole K and no activation is loaded per group.  The
 // rotation and the quantiser are those of rotate_quant_act (rotate_block.h),
 // so x_i8, a_scale and y equal the two-step result bit for bit.
-template <int NS, int GMAX, int P, int MAXT, bool ROT = false, int RS = 32, bool EARLY = false>
+//
+// TH = 2 (16-row subtiles, more than 16 tokens): the tokens form two 16-wide
+// B operands (tokens 0-15 and 16-31), so each unpacked weight operand feeds
+// two v_mfma_i32_16x16x64_i8 and the rows of a workgroup pad to a multiple
+// of 16, not 32.
+template <int NS, int GMAX, int P, int MAXT, bool ROT = false, int RS = 32, bool EARLY = false, int TH = 1>
 __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
   static_assert(P >= 1 && P <= GMAX, "prefetch depth");
+  static_assert(TH == 1 || (TH == 2 && RS == 16 && !ROT), "token halves");
   static_assert(MAXT <= 64 * kRowsMaxWaves, "x slots are sized for 8 waves");
   static_assert(RS == 32 || RS == 16, "subtile rows");
   typedef typename std::conditional<RS == 32, v16i_t, v4i>::type acc_t;
@@ -712,8 +718,11 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
     }
 
     acc_t acc[NS];
+    acc_t acc2[TH == 2 ? NS : 1];  // TH = 2: tokens 16 .. 31
 #pragma unroll
     for (int s = 0; s < NS; ++s) acc[s] = acc_t{0};
+#pragma unroll
+    for (int s = 0; s < (TH == 2 ? NS : 1); ++s) acc2[s] = acc_t{0};
 #pragma unroll
     for (int jj = 0; jj < GMAX; ++jj) {
       RowGroup<NS, RS>& d = buf[jj % NB];
@@ -739,6 +748,7 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
         // 4 h + t for MFMA t = 0..3; RS = 16, chunk 2 h + t for MFMA t = 0, 1
         constexpr int NT = RS == 32 ? 4 : 2;
         v4i xv[NT];
+        v4i xv2[TH == 2 ? NT : 1];
         if (ROT) {
           const int8_t* xr = xs + min(j, M - 1) * (K + 16) + (g0 + min(jj, ng - 1)) * 128 + 16 * NT * h;
 #pragma unroll
@@ -748,6 +758,13 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
 #pragma unroll
           for (int t = 0; t < NT; ++t)
             xv[t] = *reinterpret_cast<const v4i*>(xr + 16 * ((NT * h + t) ^ chunk_swizzle(jr)));
+          if constexpr (TH == 2) {
+            const int jr2 = min(j + 16, kXRows - 1);
+            const int8_t* xr2 = xs + (wave * NB + jj % NB) * kXSlot + jr2 * 128;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+              xv2[t] = *reinterpret_cast<const v4i*>(xr2 + 16 * ((NT * h + t) ^ chunk_swizzle(jr2)));
+          }
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -760,8 +777,11 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
           } else {
             const uint32_t wv[2] = {d.w[s].x, d.w[s].y};
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-              acc[s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(wv[t], tab), xv[t], acc[s], 0, 0, 0);
+            for (int t = 0; t < 2; ++t) {
+              const v4i wop = unpack16(wv[t], tab);
+              acc[s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, xv[t], acc[s], 0, 0, 0);
+              if constexpr (TH == 2) acc2[s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wop, xv2[t], acc2[s], 0, 0, 0);
+            }
           }
         }
       }
@@ -778,6 +798,12 @@ __global__ __launch_bounds__(MAXT) void gemv_rows_kernel(GemvArgs a, int M) {
           const int row = RS * s + (RS == 32 ? 8 * (r >> 2) + 4 * h + (r & 3) : 4 * h + r);
           atomicAdd(&red[row * kRedStride + j], acc[s][r]);
         }
+    }
+    if (TH == 2 && j + 16 < M) {
+#pragma unroll
+      for (int s = 0; s < (TH == 2 ? NS : 1); ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) atomicAdd(&red[(RS * s + 4 * h + r) * kRedStride + j + 16], acc2[s][r]);
     }
   }
   if (scale_wave) {
@@ -831,6 +857,7 @@ struct GemvPlan {
   int rows_wgs = 0;
   int rows_p = 2;    // groups of loads in flight per wave when gmax is 5 or 17
   bool rows_early = false;  // issue a group's successor before computing it
+  int rows_th = 1;   // 2: 16-row subtiles with the tokens as two 16-wide operands
 };
 
 // From this many tokens on, the matrix-core kernel beats the dot4 kernel
@@ -928,6 +955,23 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceI
       const int64_t rmax = (N + r.rows_wgs - 1) / r.rows_wgs;
       r.rows_rs = 16;
       r.rows_ns = static_cast<int>((rmax + 15) / 16);
+    } else if (r.slices > 0 && r.gmax == 5) {
+      // more than 16 tokens on 5-group waves: 16-row subtiles with two
+      // 16-token operands where they pad the rows less than 32-row subtiles
+      // (68 rows: 80, not 96), each unpacked weight operand feeding two
+      // MFMAs.  Measured against the 32-row form, one group in flight and
+      // issued early in both (µs, alternating on one box, bit-identical y):
+      // 5120 -> 17408 10.43 -> 10.09 at M = 24, 10.20 -> 9.82 at M = 17;
+      // 5120 -> 34816 17.32 -> 16.31 at M = 24, 17.23 -> 15.66 at M = 20.
+      // Deeper prefetch was slower (three groups early: 10.80 and 20.18 at
+      // M = 24; two, not early: 10.81 and 16.76).
+      const int64_t rmax = (N + r.rows_wgs - 1) / r.rows_wgs;
+      const int ns16 = static_cast<int>((rmax + 15) / 16);
+      if (ns16 * 16 < r.rows_ns * 32 && ns16 <= 6) {
+        r.rows_rs = 16;
+        r.rows_ns = ns16;
+        r.rows_th = 2;
+      }
     }
     if (r.slices > 0) {
       // Loads in flight per wave, measured (µs, alternating on one box):
@@ -947,7 +991,7 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceI
       //   9.60 at M = 8), with 32-row subtiles slower (13.36 -> 15.08).
       const bool one_round = r.rows_wgs <= dev.cu_count;
       if (r.gmax == 5) {
-        if (r.rows_rs == 32) {
+        if (r.rows_rs == 32 || r.rows_th == 2) {
           r.rows_p = 1;
           r.rows_early = true;
         } else if (one_round) {
@@ -1028,8 +1072,31 @@ hipError_t launch_rows_ns(GemvArgs a, int M, const GemvPlan& pl, hipStream_t str
   return hipGetLastError();
 }
 
+// 16-row subtiles with two 16-token operands (TH = 2): 5-group waves, one
+// group in flight, its successor issued early (as for 32-row subtiles).
+template <int NS>
+hipError_t launch_rows_halves(GemvArgs a, int M, const GemvPlan& pl, hipStream_t stream) {
+  if (pl.nw != 8 || pl.gmax != 5 || !pl.rows_early || pl.rows_p != 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 1, 512, false, 16, true, 2>), dim3(static_cast<unsigned>(pl.rows_wgs)),
+                     dim3(512), 0, stream, a, M);
+  return hipGetLastError();
+}
+
 template <bool ROT>
 hipError_t launch_rows(GemvArgs a, int M, const GemvPlan& pl, hipStream_t stream) {
+  if constexpr (!ROT) {
+    if (pl.rows_rs == 16 && pl.rows_th == 2) {
+      switch (pl.rows_ns) {
+        case 1: return launch_rows_halves<1>(a, M, pl, stream);
+        case 2: return launch_rows_halves<2>(a, M, pl, stream);
+        case 3: return launch_rows_halves<3>(a, M, pl, stream);
+        case 4: return launch_rows_halves<4>(a, M, pl, stream);
+        case 5: return launch_rows_halves<5>(a, M, pl, stream);
+        case 6: return launch_rows_halves<6>(a, M, pl, stream);
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
   if (pl.rows_rs == 16) {
     switch (pl.rows_ns) {
       case 1: return launch_rows_ns<1, 512, ROT, 16>(a, M, pl, stream);

@@ -174,16 +174,20 @@ def test_gemv_vs_gemm_shapes(twl, M, N, K):
     _gemv_vs_gemm(twl, M, N, K)
 
 
-@pytest.mark.parametrize("M", [1, 16, 24])
+@pytest.mark.parametrize("M", [1, 16, 17, 20, 24])
 @pytest.mark.parametrize("N,K", [
     # 5-group waves (K = 5120), each depth of loads in flight the planner
     # picks: 20 and 16 rows per workgroup (all five at M <= 16), 67-68 rows
     # in 16-row subtiles (three, issued early), two rounds of workgroups (two);
-    # 32-row subtiles at M = 24 (one, issued early) on every shape;
+    # above 16 tokens one group, issued early, on every shape: 32-row
+    # subtiles where 16-row ones pad no less (16, 20, 96 rows), else 16-row
+    # subtiles with two 16-token operands (67-68 rows, 46-47 rows, and 68-69
+    # rows in two rounds of workgroups; M = 17 and 20 leave the second
+    # operand nearly empty);
     # 17-group waves (K = 17408) with 16-row subtiles (three, early); waves
     # with fewer groups than their bound (4 of 5 at K = 4096, 16 of 17 at
     # K = 16384), where the last groups' loads are clamped re-reads
-    (5120, 5120), (4096, 5120), (17407, 5120), (24577, 5120), (6000, 17408),
+    (5120, 5120), (4096, 5120), (17407, 5120), (24577, 5120), (34817, 5120), (6000, 17408),
     (12000, 4096), (5120, 16384)])
 def test_gemv_prefetch_depths(twl, M, N, K):
     _gemv_vs_gemm(twl, M, N, K)
