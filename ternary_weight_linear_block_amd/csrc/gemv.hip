@@ -983,10 +983,16 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceI
       //   issued as soon as it has landed, before it is computed ("early"),
       //   is faster: 10.59 -> 9.66 on 5120 -> 17408, 16.94 -> 15.96 on
       //   5120 -> 34816, 6.57 -> 6.45 on 5120 -> 5120 at M = 24.
-      // - With one round of workgroups and 16-row subtiles: all five at most
-      //   two subtiles (5120 -> 5120, 20 rows: 5.63 -> 5.11 at M = 1), three
-      //   early with more (5120 -> 17408: 8.51 -> 8.30 at M = 1, 9.91 ->
-      //   9.24 at M = 16).
+      // - With one round of workgroups and 16-row subtiles: all five, not
+      //   early, on one subtile (4096 rows: 4.21 against 4.28 us with three
+      //   early at M = 1); three, early, on two (5120 -> 5120, 20 rows: 5.22
+      //   -> 5.00 at M = 1, 6.08 -> 5.67 at M = 16, against all five);
+      //   with more subtiles two, early, up to 8 tokens and one above
+      //   (5120 -> 17408: 8.23 -> 7.86 at M = 1, 8.57 -> 8.21 at M = 8,
+      //   8.88 -> 8.42 at M = 12, 9.19 -> 8.65 at M = 16, against three).
+      // - Two rounds of workgroups (5120 -> 34816) with 16-row subtiles keep
+      //   two up to 8 tokens (one early: 11.43 -> 11.64 at M = 1) and one,
+      //   early, above (14.20 -> 13.58 at M = 16).
       // - 17-group waves (K = 17408) keep five; with 16-row subtiles three
       //   early are faster (5120 <- 17408: 9.71 -> 9.49 at M = 1, 9.79 ->
       //   9.60 at M = 8), with 32-row subtiles slower (13.36 -> 15.08).
@@ -996,8 +1002,11 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, GemvKind kind, const DeviceI
           r.rows_p = 1;
           r.rows_early = true;
         } else if (one_round) {
-          r.rows_p = r.rows_ns <= 2 ? 5 : 3;
-          r.rows_early = r.rows_ns > 2;
+          r.rows_p = r.rows_ns == 1 ? 5 : r.rows_ns == 2 ? 3 : (M <= 8 ? 2 : 1);
+          r.rows_early = r.rows_ns > 1;
+        } else if (M > 8) {
+          r.rows_p = 1;
+          r.rows_early = true;
         }
       } else if (r.gmax == 17 && r.rows_rs == 16 && one_round) {
         r.rows_p = 3;
@@ -1029,13 +1038,15 @@ hipError_t launch_rows_ns(GemvArgs a, int M, const GemvPlan& pl, hipStream_t str
     case 5:
       if constexpr (!ROT) {
         if (pl.rows_early) {
-          if constexpr (RS == 32) {
-            if (pl.rows_p == 1) {
-              hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 1, MAXT, false, RS, true>), grid, block, 0, stream, a, M);
+          if (pl.rows_p == 1) {
+            hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 1, MAXT, false, RS, true>), grid, block, 0, stream, a, M);
+            break;
+          }
+          if constexpr (RS == 16) {
+            if (pl.rows_p == 2) {
+              hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 2, MAXT, false, RS, true>), grid, block, 0, stream, a, M);
               break;
             }
-          }
-          if constexpr (RS == 16 && NS >= 3) {
             if (pl.rows_p == 3) {
               hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 3, MAXT, false, RS, true>), grid, block, 0, stream, a, M);
               break;
@@ -1043,14 +1054,15 @@ hipError_t launch_rows_ns(GemvArgs a, int M, const GemvPlan& pl, hipStream_t str
           }
           return hipErrorInvalidValue;
         }
-        if constexpr (RS == 16 && NS <= 2) {
+        if constexpr (RS == 16 && NS == 1) {
           if (pl.rows_p == 5) {
             hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 5, MAXT, false, RS>), grid, block, 0, stream, a, M);
             break;
           }
         }
       }
-      // the fused kernels keep two groups in flight (their x_i8 fills the LDS)
+      // two groups in flight, not early: two rounds of workgroups up to 8
+      // tokens, and the fused kernels (their x_i8 fills the LDS)
       hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 2, MAXT, ROT, RS>), grid, block, 0, stream, a, M);
       break;
     case 9: hipLaunchKernelGGL((gemv_rows_kernel<NS, 9, PM, MAXT, ROT, RS>), grid, block, 0, stream, a, M); break;
