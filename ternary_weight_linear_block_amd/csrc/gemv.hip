@@ -1061,8 +1061,15 @@ hipError_t launch_rows_ns(GemvArgs a, int M, const GemvPlan& pl, hipStream_t str
           }
         }
       }
+      // the fused kernels (their x_i8 fills the LDS) on at most two subtiles:
+      // two groups, early (5120 -> 5120: 7.24 -> 7.00 us at M = 1, 8.23 ->
+      // 7.97 at M = 2; one early, or two early on more subtiles, was slower)
+      if constexpr (ROT && NS <= 2) {
+        hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 2, MAXT, ROT, RS, true>), grid, block, 0, stream, a, M);
+        break;
+      }
       // two groups in flight, not early: two rounds of workgroups up to 8
-      // tokens, and the fused kernels (their x_i8 fills the LDS)
+      // tokens, and the other fused kernels
       hipLaunchKernelGGL((gemv_rows_kernel<NS, 5, 2, MAXT, ROT, RS>), grid, block, 0, stream, a, M);
       break;
     case 9: hipLaunchKernelGGL((gemv_rows_kernel<NS, 9, PM, MAXT, ROT, RS>), grid, block, 0, stream, a, M); break;

@@ -552,6 +552,8 @@ def test_plan_info_matches_workspace_and_family(twl, M, N, K, path, family):
     (1, 17408, 5120, False, True),   # decode gate/up: 5 blocks over 8 waves
     (2, 17408, 5120, True, True),    # the SiLU form, 10 blocks
     (2, 16001, 2048, False, True),   # ragged rows (62-63 per workgroup), 4 blocks
+    (1, 5120, 5120, False, True),    # 20 rows per workgroup: two subtiles, loads issued early
+    (2, 5120, 5120, True, True),
     (1, 5120, 17408, True, True),    # decode down with its SiLU input: 17 blocks
     (1, 5120, 17408, False, True),
     (1, 8000, 9216, True, True),     # 31-32 rows per workgroup, 9 groups per wave
