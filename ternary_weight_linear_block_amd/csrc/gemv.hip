@@ -1195,13 +1195,20 @@ hipError_t launch_gemv(const int8_t* x_i8, const float* a_scale, const uint8_t* 
   if (pl.slices <= 0 || (kind == kGemvMfma && !pl.mfma)) return hipErrorInvalidValue;
   if (pl.slices > 1 && (part == nullptr || part_bytes < gemv_workspace_bytes(M, N, K, kind, dev)))
     return hipErrorInvalidValue;
-  if (std::getenv("TWL_LOG"))
+  if (std::getenv("TWL_LOG")) {
+    // the row kernel's form: subtiles, token operands, groups of loads in
+    // flight per wave (as launch_rows_ns dispatches them) and early issue
+    char form[96] = "";
+    if (pl.rows_ns > 0) {
+      const int depth = pl.gmax == 3 ? 3 : (pl.gmax == 5 || (pl.gmax == 17 && pl.rows_early)) ? pl.rows_p : 5;
+      std::snprintf(form, sizeof(form), ", %d-row subtiles x%d%s, %d in flight%s", pl.rows_rs, pl.rows_ns,
+                    pl.rows_th == 2 ? " (two 16-token operands)" : "", depth, pl.rows_early ? ", early" : "");
+    }
     std::fprintf(stderr, "[twl] gemv%s M=%lld N=%lld K=%lld -> <= %d groups/wave, %d waves/WG, %d slices, grid=%d%s\n",
                  pl.rows_ns > 0 ? "-rows" : (pl.mfma ? "-mfma" : ""), static_cast<long long>(M),
                  static_cast<long long>(N), static_cast<long long>(K), pl.gmax, pl.nw, pl.slices,
-                 pl.rows_ns > 0 ? pl.rows_wgs : pl.n_rb * pl.slices,
-                 pl.rows_ns > 0 && pl.rows_early ? (pl.rows_p == 1 ? ", 1 in flight, early" : ", 3 in flight, early")
-                 : pl.rows_ns > 0 && pl.gmax == 5 ? (pl.rows_p == 5 ? ", 5 in flight" : ", 2 in flight") : "");
+                 pl.rows_ns > 0 ? pl.rows_wgs : pl.n_rb * pl.slices, form);
+  }
   GemvArgs a = {};
   a.x = x_i8;
   a.a_scale = a_scale;
