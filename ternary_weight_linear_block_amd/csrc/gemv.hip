@@ -35,9 +35,10 @@
 //   v_mfma_i32_32x32x32_i8 (in gemv_rows_kernel at up to 16 tokens: padded to
 //   16, v_mfma_i32_16x16x64_i8; above 16 tokens, where 16-row subtiles pad the
 //   rows less, two 16-token operands of that instruction) and the unpacked
-//   weights the A operand, which makes the work nearly independent of M.  gemv_rows_kernel gives every CU an
-//   equal contiguous range of rows over all of K (no partial sums leave the
-//   workgroup) and is used at every M whenever each CU gets at least 16 rows;
+//   weights the A operand, which makes the work nearly independent of M.
+//   gemv_rows_kernel gives every CU an equal contiguous range of rows over all
+//   of K (no partial sums leave the workgroup) and is used at every M whenever
+//   each CU gets at least 16 rows;
 //   gemv_mfma_kernel keeps the 64-row-block split with K slices (4 <= M <= 24)
 //   for layers with fewer rows per CU.
 #include "rotate_block.h"
