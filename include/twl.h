@@ -258,6 +258,12 @@ twl_status twl_ternary_linear_noalloc(const int8_t* x_i8, const float* a_scale,
  * M = 0 or N = 0 writes zeros.  Errors as twl_ternary_linear_ex (shape, path,
  * decode batch limit), TWL_EINVAL for a NULL info, TWL_EDEVICE / TWL_EHIP
  * when the current device is not a usable gfx950.
+ *
+ * Diagnostics: with the environment variable TWL_LOG set, every launching
+ * call also prints its plan on stderr, one line beginning "[twl]" (for the
+ * decode row kernel including its subtile form, token operands, groups of
+ * loads in flight per wave and early issue).  The format is for people and
+ * tests, not a stable interface.
  */
 twl_status twl_plan_info(int64_t M, int64_t N, int64_t K, int path, int64_t* info);
 
