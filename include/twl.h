@@ -259,8 +259,9 @@ twl_status twl_ternary_linear_noalloc(const int8_t* x_i8, const float* a_scale,
  * decode batch limit), TWL_EINVAL for a NULL info, TWL_EDEVICE / TWL_EHIP
  * when the current device is not a usable gfx950.
  *
- * Diagnostics: with the environment variable TWL_LOG set, every launching
- * call also prints its plan on stderr, one line beginning "[twl]" (for the
+ * Diagnostics: with the environment variable TWL_LOG set, every linear call
+ * (ternary_linear and its variants, rotate_quant_linear) also prints its plan
+ * on stderr, one line beginning "[twl]" (for the
  * decode row kernel including its subtile form, token operands, groups of
  * loads in flight per wave and early issue).  The format is for people and
  * tests, not a stable interface.
