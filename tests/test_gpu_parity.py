@@ -167,7 +167,9 @@ def test_gemm_ragged_shapes(twl, M, N, K):
                                  (4100, 3072), (8000, 9216),
                                  # up to 16 tokens, 16-row subtiles: 16 rows per
                                  # workgroup (one subtile), 62-63 rows (four)
-                                 (4096, 2048), (16000, 1024)])
+                                 (4096, 2048), (16000, 1024),
+                                 # five rounds of workgroups, 78-79 rows each
+                                 (100003, 1024)])
 def test_gemv_vs_gemm_shapes(twl, M, N, K):
     # every decode kernel (automatic choice, dot4, MFMA) and the GEMM against
     # the oracle, bit-exact in acc
