@@ -157,6 +157,24 @@ def test_gemm_ragged_shapes(twl, M, N, K):
     _check_linear(twl, x_i8, a_scale, packed, q, smax, layer.code, oq, osm, 1, f"ragged {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (511, 17408, 1024),   # last row tile one row short
+    (449, 34816, 2048),   # last row tile of 65 rows; two rounds of workgroups
+    (1000, 24580, 1024),  # ragged rows and columns (N % 8 == 4)
+    (1000, 8704, 1024)])
+def test_gemm_12_wave_tile_ragged(twl, M, N, K):
+    # the 128 x 288 tile of 12 waves (the prefill gate/up plan) with M and N
+    # not multiples of the tile, as the planner picks it for these shapes
+    plan = twl.plan_info(M, N, K)
+    assert (plan["family"], plan["tile_rows"], plan["tile_cols"], plan["waves"], plan["splits"]) == \
+        ("gemm", 128, 288, 12, 1), plan
+    layer = W.make_layer(9000 + M + N, M, K, N)
+    x_i8, a_scale = O.rotate_quant_act(layer.x_bits, layer.sign)
+    packed, q, smax, oq, osm = _check_pack(twl, layer.code, layer.s_bits, "12-wave ragged")
+    _check_linear(twl, x_i8, a_scale, packed, q, smax, layer.code, oq, osm, twl.PATH_AUTO,
+                  f"12-wave ragged {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 13, 17, 24])
 @pytest.mark.parametrize("N,K", [(1, 1024), (65, 2048), (1000, 5120),
                                  # row-balanced decode: 40-41 rows per workgroup,
